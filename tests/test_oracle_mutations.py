@@ -1,0 +1,94 @@
+"""The oracle's pins must catch plausible mistakes in the oracle itself.
+
+Each case copies ``oracle/gemm_ref.c``, plants one mistake by a textual
+substitution, builds the copy with gcc and runs the pin checks against it on
+the CPU; at least one pin has to fail.  Every planted mistake keeps all
+memory accesses in bounds.
+"""
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+from dense_fp16_gemm_f16_amd import inputs
+from tests import pins
+from tests._exact import exact_gemm_bits
+from tests.test_oracle_gemm import _rand_f16
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "gemm_ref.c")
+
+MUTANTS = {
+    "drop_last_k_term": ("ki < j->k; ++ki", "ki + 1 < j->k; ++ki"),
+    "subtract_products": ("sum += j->table", "sum -= j->table"),
+    "b_read_as_k_by_n": ("j->table[brow[ki]]", "j->table[j->b[(ki * j->n + ni) % (j->n * j->k)]]"),
+    "wrong_a_row": ("arow = j->a + mi * j->k", "arow = j->a + ((mi + 1) % j->m) * j->k"),
+    "round_via_fp32": ("oracle_f64_to_f16(sum)", "oracle_f64_to_f16((double)(float)sum)"),
+    "ties_away_from_zero": ("return (fmod(fl, 2.0) == 0.0) ? fl : fl + 1.0;", "return fl + 1.0;"),
+    "subnormal_scale": ("ldexp(ax, 24)", "ldexp(ax, 23)"),
+    "decode_bias": ("ldexp((double)(1024 + f), e - 25)", "ldexp((double)(1024 + f), e - 24)"),
+    "subnormal_threshold": ("if (e < -14)", "if (e < -15)"),
+}
+
+
+def _pin_failures(orc):
+    fails = []
+    rng = np.random.default_rng(123)
+    for (m, n, k) in [(3, 4, 9), (8, 8, 16)]:
+        a = _rand_f16(rng, (m, k), -6, 6)
+        b = _rand_f16(rng, (n, k), -6, 6)
+        if not np.array_equal(orc.gemm_f16_nt(a, b).view(np.uint16),
+                              exact_gemm_bits(a.view(np.uint16), b.view(np.uint16))):
+            fails.append("brute_force")
+    sub = (rng.integers(-1023, 1024, size=(3, 9)) * 2.0**-24).astype(np.float16)
+    b = _rand_f16(rng, (4, 9), -6, 6)
+    if not np.array_equal(orc.gemm_f16_nt(sub, b).view(np.uint16),
+                          exact_gemm_bits(sub.view(np.uint16), b.view(np.uint16))):
+        fails.append("subnormal")
+    a = np.array([[1.0, 2.0**-11], [1.0, 3 * 2.0**-11]], dtype=np.float16)
+    c = orc.gemm_f16_nt(a, np.array([[1.0, 1.0]], dtype=np.float16)).view(np.uint16)
+    if c[0, 0] != 0x3C00 or c[1, 0] != 0x3C02:
+        fails.append("ties_to_even")
+    a = np.array([[1.0, 2.0**-11, 2.0**-15]], dtype=np.float16)
+    b = np.array([[1.0, 1.0, 2.0**-15]], dtype=np.float16)
+    if orc.gemm_f16_nt(a, b).view(np.uint16)[0, 0] != 0x3C01:
+        fails.append("double_rounding")
+    a = np.array([[255.875, 255.875], [255.875, 0.0]], dtype=np.float16)
+    b = np.array([[255.875, 255.875], [255.875, 0.25]], dtype=np.float16)
+    c = orc.gemm_f16_nt(a, b).view(np.uint16)
+    if c[0, 0] != 0x7C00:
+        fails.append("overflow")
+    a = np.array([[2047.0, 1.0]], dtype=np.float16)
+    b = np.array([[32.0, 16.0]], dtype=np.float16)  # 65504 + 16 = 65520: the overflow tie
+    if orc.gemm_f16_nt(a, b).view(np.uint16)[0, 0] != 0x7C00:
+        fails.append("overflow_tie")
+    for k in (1000, 4096):
+        if not np.all(orc.gemm_f16_nt(np.ones((2, k), np.float16), np.ones((3, k), np.float16))
+                      == np.float16(k)):
+            fails.append("all_ones")
+    ae, be = inputs.workload_inputs("gemm_256_eighths")
+    if not np.array_equal(orc.gemm_f16_nt(ae, be).view(np.uint16), pins.eighths_exact_bits(ae, be)):
+        fails.append("eighths_exact")
+    # the converter itself, against numpy's float64 -> float16 on a sweep
+    xs = np.concatenate([np.exp2(np.linspace(-26, 16.5, 4001)), [65519.0, 65520.0, 2.0**-15 * 1.3]])
+    got = np.array([orc.f64_to_f16(float(x)) for x in xs], dtype=np.uint16)
+    with np.errstate(over="ignore"):
+        if not np.array_equal(got, xs.astype(np.float16).view(np.uint16)):
+            fails.append("converter_sweep")
+    return fails
+
+
+def test_unmutated_oracle_passes_every_pin():
+    assert _pin_failures(oracle._load()) == []
+
+
+@pytest.mark.parametrize("name", sorted(MUTANTS))
+def test_planted_mistake_is_caught(name, tmp_path):
+    old, new = MUTANTS[name]
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation site for {name} not unique"
+    path = tmp_path / "gemm_ref_mutant.c"
+    path.write_text(src.replace(old, new))
+    lib = oracle.build(str(path), str(tmp_path / f"lib_{name}.so"))
+    fails = _pin_failures(oracle.Oracle(lib))
+    assert fails, f"planted mistake {name} passed every pin"
