@@ -1,0 +1,205 @@
+#!/usr/bin/env python3
+"""Throughput of the fp16 GEMM C = fp16(A @ B^T) (fp32 accumulate) on one MI355X.
+
+One step is one GEMM over the whole workload (default: M = N = K = 8192,
+A and B i.i.d. uniform[-1,1] rounded to fp16), with A, B and C resident in
+HBM before the timed region starts.  Prints one JSON line.
+
+Timing follows the tutorials' protocol (CUDA-event timed; the Tilus pages
+report the median of three fresh processes): W untimed warm-up GEMMs, then
+exactly K timed GEMMs between two device synchronisations; every launch is
+also bracketed by HIP events on the stream it runs on, which gives the
+kernel's average duration for the roofline figure.
+
+The CPU baseline times the oracle (plain fp64 triple loop, one fp16
+rounding) on a bounded sample of the same workload -- whole rows of C -- and
+the same rows double as a parity spot check of the timed output.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "fp16 GEMM TFLOP/s (fp32 acc) at 8192³; % of MI355X dense fp16 MFMA peak"
+PEAK_TFLOPS = 2500.0  # MI355X dense fp16 MFMA, published
+KERNEL_SRC = os.path.join(ROOT, "dense_fp16_gemm_f16_amd", "csrc", "gemm_f16.hip")
+PROFILE_DIR = os.path.join(ROOT, "profiles")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in ("gemm_f16.hip", "tile_sched.h"):
+        with open(os.path.join(os.path.dirname(KERNEL_SRC), name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter runs, if they
+    were taken on the current kernel source; else None."""
+    path = os.path.join(PROFILE_DIR, f"traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(a, b, c_gpu, w, budget_s: float):
+    """Time the oracle on whole rows of C; returns (record, parity summary)."""
+    import numpy as np
+
+    import oracle
+
+    threads = oracle.default_threads()
+    rng = np.random.default_rng(12345)
+    # calibrate on one row, then size the sample to the time budget
+    t0 = time.perf_counter()
+    first = oracle.gemm_f16_nt_rows(a, b, [0], threads)
+    t_one = max(time.perf_counter() - t0, 1e-6)
+    rows_fit = int(budget_s / t_one)
+    nrows = max(threads, min(w.m, (rows_fit // threads) * threads or threads))
+    rows = np.sort(rng.choice(w.m, size=min(nrows, w.m), replace=False))
+    t0 = time.perf_counter()
+    ref = oracle.gemm_f16_nt_rows(a, b, rows, threads)
+    dt = time.perf_counter() - t0
+    flops = 2.0 * len(rows) * w.n * w.k
+    rec = {
+        "value": round(flops / dt / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"{len(rows)} of {w.m} rows of C (all {w.n} columns, full K={w.k}), "
+                  f"fp64 triple loop, {dt:.1f} s",
+    }
+    got = c_gpu[rows].astype(np.float64)
+    r = ref.astype(np.float64)
+    # 2 fp16 ulp of |C_oracle| + 1e-2 sqrt(K) 2^-11 (bit-exact expected on {-8..8}/8)
+    ar = np.abs(r)
+    e = np.where(ar > 0, np.maximum(np.floor(np.log2(np.where(ar > 0, ar, 1.0))), -14), -14)
+    tol = 2.0 * np.exp2(e - 10) + 1e-2 * np.sqrt(w.k) * 2.0**-11
+    if w.dist == "eighths":
+        tol = np.zeros_like(tol) + 1e-300
+    err = np.abs(got - r)
+    err = np.where(np.isnan(err), np.inf, err)
+    worst = float(np.max(err / tol)) if err.size else 0.0
+    ok = worst <= 1.0
+    del first
+    return rec, {"rows": int(len(rows)), "ok": bool(ok), "worst_err_over_tol": round(worst, 4)}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="gemm_8192_uniform")
+    ap.add_argument("--tile", type=int, default=0)
+    ap.add_argument("--swizzle", type=int, default=0)
+    ap.add_argument("--xcd", type=int, default=-1)
+    ap.add_argument("--cpu-budget", type=float, default=15.0,
+                    help="seconds of oracle work for the CPU baseline (0 = skip)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only: this GEMM has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}).", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import dense_fp16_gemm_f16_amd as g
+    from dense_fp16_gemm_f16_amd import inputs
+
+    w = inputs.WORKLOADS[args.workload]
+    print(f"[bench] workload {w.name} ({w.m}x{w.n}x{w.k}, {w.dist}); generating inputs",
+          file=sys.stderr, flush=True)
+    a_np, b_np = inputs.workload_inputs(w.name)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    a = torch.from_numpy(a_np).to(dev)
+    b = torch.from_numpy(b_np).to(dev)
+    c = torch.empty((w.m, w.n), dtype=torch.float16, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+    ap_, bp_, cp_ = a.data_ptr(), b.data_ptr(), c.data_ptr()
+
+    def step():
+        rc = g.gemm_f16_nt_raw(w.m, w.n, w.k, ap_, bp_, cp_, sp, args.tile, args.swizzle, args.xcd)
+        if rc != g.OK:
+            raise g.GemmError(rc)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print(f"[bench] warmup {args.warmup} done; timing {args.steps} steps", file=sys.stderr, flush=True)
+
+    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        starts[i].record(stream)
+        step()
+        ends[i].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    durs = [s.elapsed_time(e) for s, e in zip(starts, ends)]  # ms
+    avg_ms = sum(durs) / len(durs)
+    med_ms = sorted(durs)[len(durs) // 2]
+    ms_per_step = wall * 1e3 / args.steps
+    flops = float(w.flops)
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    achieved = flops / (avg_ms * 1e-3) / 1e12
+    print(f"[bench] kernel avg {avg_ms * 1e3:.1f} us, median {med_ms * 1e3:.1f} us, "
+          f"wall/step {ms_per_step * 1e3:.1f} us", file=sys.stderr, flush=True)
+
+    rec = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16 (fp32 accumulate)",
+        "data": "synthetic",
+        "config": {"workload": w.name, "m": w.m, "n": w.n, "k": w.k, "values": w.dist,
+                   "tile": args.tile or g.select_tile(w.m, w.n, w.k)},
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_TFLOPS, 4),
+            "traffic": measured_traffic(w.name),
+            "kernel_avg_us": round(avg_ms * 1e3, 2),
+            "kernel_median_us": round(med_ms * 1e3, 2),
+        },
+        "cpu_baseline": None,
+    }
+    if args.cpu_budget > 0:
+        print("[bench] CPU baseline (oracle on sampled rows)", file=sys.stderr, flush=True)
+        c_host = c.cpu().numpy()
+        base, parity = cpu_baseline(a_np, b_np, c_host, w, args.cpu_budget)
+        rec["cpu_baseline"] = base
+        rec["parity_sample"] = parity
+    print(json.dumps(rec), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

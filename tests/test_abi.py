@@ -1,0 +1,108 @@
+"""The C-ABI library loads, exports what include/gemm_f16.h declares, and its
+host logic (argument checks, status strings, tile scheduler, tile choice)
+behaves as documented.  No GPU is needed: every call here returns before the
+library makes its first HIP call.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import dense_fp16_gemm_f16_amd as g
+from oracle import raster
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gemm_f16.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gemm_f16_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    declared = _declared_functions()
+    assert declared == sorted(g.EXPORTS)
+    L = g.lib()
+    for name in declared:
+        assert hasattr(L, name), name
+
+
+def test_status_strings():
+    for code in (g.OK, g.EINVAL, g.ENULL, g.EALIGN, g.EDEVICE, g.EHIP, g.EOVERLAP):
+        s = g.status_string(code)
+        assert s and s != "unknown status"
+    assert g.status_string(-99) == "unknown status"
+
+
+FAKE_A, FAKE_B, FAKE_C = 0x10000000, 0x20000000, 0x30000000  # never dereferenced
+
+
+@pytest.mark.parametrize(
+    "args, expect",
+    [
+        ((-1, 4, 4, FAKE_A, FAKE_B, FAKE_C), g.EINVAL),
+        ((4, -1, 4, FAKE_A, FAKE_B, FAKE_C), g.EINVAL),
+        ((4, 4, -1, FAKE_A, FAKE_B, FAKE_C), g.EINVAL),
+        ((4, 4, 1 << 22, FAKE_A, FAKE_B, FAKE_C), g.EINVAL),
+        ((1 << 31, 4, 4, FAKE_A, FAKE_B, FAKE_C), g.EINVAL),
+        ((4, 4, 4, 0, FAKE_B, FAKE_C), g.ENULL),
+        ((4, 4, 4, FAKE_A, 0, FAKE_C), g.ENULL),
+        ((4, 4, 4, FAKE_A, FAKE_B, 0), g.ENULL),
+        ((4, 4, 4, FAKE_A + 1, FAKE_B, FAKE_C), g.EALIGN),
+        ((4, 4, 4, FAKE_A, FAKE_B, FAKE_C + 1), g.EALIGN),
+        ((4, 4, 4, FAKE_A, FAKE_B, FAKE_A + 8), g.EOVERLAP),
+        ((4, 4, 4, FAKE_A, FAKE_B, FAKE_B - 8), g.EOVERLAP),
+        ((0, 4, 4, FAKE_A, FAKE_B, FAKE_C), g.OK),   # empty: nothing launched
+        ((4, 0, 4, FAKE_A, FAKE_B, FAKE_C), g.OK),
+        ((0, 0, 0, 0, 0, 0), g.OK),
+    ],
+)
+def test_argument_checks_return_before_any_hip_call(args, expect):
+    assert g.lib().gemm_f16_nt(*args, None) == expect
+
+
+@pytest.mark.parametrize("opt", [(4, 0, -1), (-1, 0, -1), (0, -1, -1), (0, 0, 2), (0, 0, -2)])
+def test_bad_options_rejected(opt):
+    assert g.gemm_f16_nt_raw(8, 8, 8, FAKE_A, FAKE_B, FAKE_C, 0, *opt) == g.EINVAL
+
+
+@pytest.mark.parametrize("nm,nn", [(1, 1), (3, 5), (8, 8), (32, 32), (64, 16), (20, 12), (17, 31)])
+@pytest.mark.parametrize("sw", [1, 3, 4, 8])
+@pytest.mark.parametrize("xcd", [0, 1])
+def test_tile_coord_matches_the_oracle(nm, nn, sw, xcd):
+    grid = nm * nn
+    seen = set()
+    for pid in range(grid):
+        logical = raster.xcd_remap(pid, grid, 8) if xcd else pid
+        expect = raster.swizzle_tile_coord(logical, nm, nn, sw)
+        got = g.tile_coord(pid, nm, nn, sw, xcd)
+        assert got == expect
+        seen.add(got)
+    assert len(seen) == grid
+
+
+def test_tile_coord_rejects_bad_input():
+    for args in [(-1, 4, 4, 1, 0), (16, 4, 4, 1, 0), (0, 4, 4, 0, 0), (0, 0, 4, 1, 0)]:
+        with pytest.raises(g.GemmError):
+            g.tile_coord(*args)
+
+
+def test_select_tile():
+    assert g.select_tile(8192, 8192, 8192) == g.TILE_256x256
+    assert g.select_tile(4096, 4096, 4096) == g.TILE_256x256   # 256 tiles: one per CU
+    assert g.select_tile(256, 256, 256) == g.TILE_64x64
+    assert g.select_tile(5000, 3000, 1000) in g.TILES
+    with pytest.raises(g.GemmError):
+        g.select_tile(-1, 4, 4)
+
+
+def test_python_wrapper_refuses_cpu_tensors():
+    torch = pytest.importorskip("torch")
+    a = torch.zeros(4, 8, dtype=torch.float16)
+    with pytest.raises(ValueError):
+        g.gemm_f16_nt(a, a)
+    with pytest.raises(TypeError):
+        g.gemm_f16_nt(a.float(), a.float())

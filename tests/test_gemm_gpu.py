@@ -1,0 +1,221 @@
+"""Parity of the HIP GEMM against the CPU oracle, through the C ABI.
+
+Bars (written here, from the method's arithmetic):
+* {-8..8}/8 inputs and the closed forms: bit-exact.  Every partial sum of
+  those inputs is a multiple of 1/64 far below 2^24, so fp32 accumulation is
+  exact in any order and the one fp16 rounding (to nearest, ties to even)
+  has a unique result; this is stricter than the 1e-3 relative gate of
+  "wgmma_gemm.cu" (day 78), which is checked as well.
+* N(0,1), N(0,0.5), uniform[-1,1] inputs: |C - C_oracle| <= 2 ulp_fp16(|C_oracle|)
+  + 1e-2 sqrt(K) 2^-11 per element.
+"""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import dense_fp16_gemm_f16_amd as g  # noqa: E402
+import oracle  # noqa: E402
+from dense_fp16_gemm_f16_amd import inputs  # noqa: E402
+from tests import pins  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+GUARD = 64  # fp16 elements of sentinel on each side of C
+SENTINEL = 0x7E5A  # a NaN pattern the kernel never produces
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    g.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+def _announce(*what):
+    print("case:", *what, flush=True)
+
+
+def run_gemm(a_np, b_np, a_offset=0, b_offset=0, **opts):
+    """C from the HIP path; A/B may be placed `offset` elements past an aligned
+    base to exercise the unaligned loader.  C sits between guard bands."""
+    m, k = a_np.shape
+    n = b_np.shape[0]
+    dev = torch.device("cuda")
+    a_buf = torch.zeros(a_offset + m * k + 8, dtype=torch.float16, device=dev)
+    b_buf = torch.zeros(b_offset + n * k + 8, dtype=torch.float16, device=dev)
+    if m * k:
+        a_buf[a_offset:a_offset + m * k] = torch.from_numpy(a_np.reshape(-1)).to(dev)
+    if n * k:
+        b_buf[b_offset:b_offset + n * k] = torch.from_numpy(b_np.reshape(-1)).to(dev)
+    c_buf = torch.full((GUARD + m * n + GUARD,), SENTINEL, dtype=torch.int16, device=dev)
+    stream = torch.cuda.current_stream()
+    rc = g.gemm_f16_nt_raw(m, n, k, a_buf.data_ptr() + 2 * a_offset, b_buf.data_ptr() + 2 * b_offset,
+                           c_buf.data_ptr() + 2 * GUARD, stream.cuda_stream, **opts)
+    assert rc == g.OK, g.status_string(rc)
+    torch.cuda.synchronize()
+    host = c_buf.cpu().numpy().view(np.uint16)
+    assert np.all(host[:GUARD] == SENTINEL) and np.all(host[GUARD + m * n:] == SENTINEL), \
+        "write outside C"
+    return host[GUARD:GUARD + m * n].reshape(m, n).view(np.float16)
+
+
+def assert_bits_equal(got, ref, what):
+    gb, rb = got.view(np.uint16), ref.view(np.uint16)
+    bad = np.argwhere(gb != rb)
+    assert bad.size == 0, (f"{what}: {len(bad)} mismatches, first at {tuple(bad[0])}: "
+                           f"gpu {got[tuple(bad[0])]} oracle {ref[tuple(bad[0])]}")
+
+
+def assert_ulp(got, ref, k, what):
+    ok, worst, idx = pins.check_ulp(got, ref, k)
+    assert ok, f"{what}: worst |err|/tol = {worst:.3f} at {idx}: gpu {got[idx]} oracle {ref[idx]}"
+
+
+TILES = sorted(g.TILES)
+
+
+def normal_f16(rng, shape):
+    """N(0,1) rounded to fp16, with magnitudes below 2^-10 pushed to 2^-10 so
+    the bit-exact layout checks do not depend on fp16 subnormal handling."""
+    x = rng.standard_normal(shape)
+    x = np.where(np.abs(x) < 2.0**-10, np.copysign(2.0**-10, x), x)
+    return x.astype(np.float16)
+
+
+@pytest.mark.parametrize("tile", TILES)
+def test_one_hot_rows_place_fragments(tile):
+    """A[m, p(m)] = 1, else 0  =>  C[m, n] = B[n, p(m)] exactly: pins the MFMA
+    operand and result layouts and the LDS swizzle for every tile shape."""
+    _announce("one_hot", tile)
+    rng = np.random.default_rng(20 + tile)
+    m, n, k = 300, 270, 192
+    p = rng.integers(0, k, size=m)
+    a = np.zeros((m, k), dtype=np.float16)
+    a[np.arange(m), p] = 1.0
+    b = normal_f16(rng, (n, k))
+    got = run_gemm(a, b, tile=tile)
+    assert_bits_equal(got, b[:, p].T.copy(), "one-hot")
+
+
+@pytest.mark.parametrize("tile", TILES)
+def test_identity_and_all_ones(tile):
+    _announce("identity/all-ones", tile)
+    rng = np.random.default_rng(30 + tile)
+    k = 256
+    b = normal_f16(rng, (200, k))
+    got = run_gemm(np.eye(k, dtype=np.float16), b, tile=tile)
+    assert_bits_equal(got, b.T.copy(), "A = I")
+    a = normal_f16(rng, (77, k))
+    assert_bits_equal(run_gemm(a, np.eye(k, dtype=np.float16), tile=tile), a, "B = I")
+    ones = run_gemm(np.ones((70, 1000), np.float16), np.ones((90, 1000), np.float16), tile=tile)
+    assert np.all(ones == np.float16(1000))
+
+
+@pytest.mark.parametrize("name", ["gemm_256_eighths", "gemm_5000x3000x1000_eighths"])
+def test_eighths_workloads_bit_exact(name):
+    _announce(name)
+    a, b = inputs.workload_inputs(name)
+    got = run_gemm(a, b)
+    ref = oracle.gemm_f16_nt(a, b)
+    assert_bits_equal(got, ref, name)
+    assert_bits_equal(got, pins.eighths_exact_bits(a, b).view(np.float16), name + " (exact)")
+    ok, worst, idx = pins.check_rel(got, ref, 1e-3)
+    assert ok, f"rel {worst} at {idx}"
+
+
+def test_4096_normal_full_oracle():
+    _announce("gemm_4096_normal")
+    a, b = inputs.workload_inputs("gemm_4096_normal")
+    got = run_gemm(a, b)
+    assert_ulp(got, oracle.gemm_f16_nt(a, b), 4096, "gemm_4096_normal")
+
+
+def _rows_one_per_tile(m, bm=256):
+    rows = {0, m - 1}
+    for t in range((m + bm - 1) // bm):
+        rows.add(min(m - 1, t * bm + (t * 37 + 11) % bm))
+    return sorted(rows)
+
+
+@pytest.mark.parametrize("name", ["gemm_8192_uniform", "gemm_16384x4096x2048_normal05"])
+def test_large_workloads_sampled_rows(name):
+    """Full-size runs in the default launch configuration; the oracle computes
+    one row per 256-row block tile (all N columns, full K)."""
+    _announce(name)
+    w = inputs.WORKLOADS[name]
+    a, b = inputs.workload_inputs(name)
+    got = run_gemm(a, b)
+    assert np.all(np.isfinite(got.astype(np.float32)))
+    rows = _rows_one_per_tile(w.m)
+    ref = oracle.gemm_f16_nt_rows(a, b, rows)
+    assert_ulp(got[rows], ref, w.k, name)
+
+
+RAGGED = [
+    (1, 1, 1), (1, 1, 8), (7, 5, 3), (31, 33, 17), (33, 31, 64), (64, 64, 64), (65, 63, 72),
+    (129, 200, 136), (255, 257, 1000), (257, 255, 520), (300, 70, 7), (513, 130, 65),
+]
+
+
+@pytest.mark.parametrize("m,n,k", RAGGED)
+@pytest.mark.parametrize("tile", TILES)
+def test_ragged_shapes(m, n, k, tile):
+    _announce("ragged", m, n, k, tile)
+    rng = np.random.default_rng(m * 7 + n * 13 + k)
+    a = rng.standard_normal((m, k)).astype(np.float16)
+    b = rng.standard_normal((n, k)).astype(np.float16)
+    assert_ulp(run_gemm(a, b, tile=tile), oracle.gemm_f16_nt(a, b), k, f"{m}x{n}x{k}")
+
+
+@pytest.mark.parametrize("a_off,b_off", [(1, 0), (0, 3), (5, 7)])
+def test_unaligned_operands_take_the_scalar_loader(a_off, b_off):
+    _announce("unaligned", a_off, b_off)
+    rng = np.random.default_rng(a_off * 10 + b_off)
+    m, n, k = 150, 140, 96
+    a = (rng.integers(-8, 9, size=(m, k)) / 8).astype(np.float16)
+    b = (rng.integers(-8, 9, size=(n, k)) / 8).astype(np.float16)
+    got = run_gemm(a, b, a_offset=a_off, b_offset=b_off)
+    assert_bits_equal(got, oracle.gemm_f16_nt(a, b), "unaligned")
+
+
+def test_k_zero_writes_zeros_and_empty_is_a_no_op():
+    _announce("degenerate")
+    got = run_gemm(np.zeros((37, 0), np.float16), np.zeros((45, 0), np.float16))
+    assert np.all(got.view(np.uint16) == 0)
+    assert run_gemm(np.zeros((0, 16), np.float16), np.ones((9, 16), np.float16)).shape == (0, 9)
+    assert run_gemm(np.ones((9, 16), np.float16), np.zeros((0, 16), np.float16)).shape == (9, 0)
+
+
+def test_schedule_options_do_not_change_bits():
+    """Rasterization only reorders tiles; each output's sum order is fixed."""
+    _announce("determinism")
+    rng = np.random.default_rng(99)
+    a = rng.standard_normal((2048, 640)).astype(np.float16)
+    b = rng.standard_normal((1536, 640)).astype(np.float16)
+    base = run_gemm(a, b, tile=g.TILE_256x256)
+    for sw, xcd in [(1, 0), (1, 1), (3, 1), (8, 0), (64, 1)]:
+        assert_bits_equal(run_gemm(a, b, tile=g.TILE_256x256, swizzle=sw, xcd=xcd), base, f"{sw},{xcd}")
+    assert_bits_equal(run_gemm(a, b, tile=g.TILE_256x256), base, "repeat")
+
+
+def test_torch_wrapper_on_a_side_stream():
+    _announce("stream")
+    rng = np.random.default_rng(5)
+    a = rng.standard_normal((384, 320)).astype(np.float16)
+    b = rng.standard_normal((448, 320)).astype(np.float16)
+    ta = torch.from_numpy(a).cuda()
+    tb = torch.from_numpy(b).cuda()
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        c = g.gemm_f16_nt(ta, tb)
+    s.synchronize()
+    assert_ulp(c.cpu().numpy(), oracle.gemm_f16_nt(a, b), 320, "side stream")
+
+
+def test_overlap_and_null_are_refused_on_device():
+    _announce("errors")
+    x = torch.zeros(64 * 64, dtype=torch.float16, device="cuda")
+    assert g.gemm_f16_nt_raw(64, 64, 64, x.data_ptr(), x.data_ptr(), x.data_ptr()) == g.EOVERLAP
+    assert g.gemm_f16_nt_raw(64, 64, 64, 0, x.data_ptr(), x.data_ptr()) == g.ENULL
