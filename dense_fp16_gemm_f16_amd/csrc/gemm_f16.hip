@@ -10,16 +10,18 @@
 //               XCD-aware and swizzle-rasterized (tile_sched.h);
 //  * loader     buffer_load_dwordx4 of 16-byte K-chunks (one 128-byte row
 //               segment per 8 lanes), staged in VGPRs one K-tile ahead and
-//               written to a 2-stage LDS ring; hardware range checks of the
-//               buffer descriptor return zero for rows past M/N, and a
-//               per-chunk mask returns zero for k >= K;
-//  * LDS        each row of a tile is 8 chunks of 16 bytes, stored at chunk
-//               position (c ^ swz(row)), so the ds_read_b128 fragment reads
-//               of the MFMA loop and the ds_write_b128 stores are free of
-//               bank conflicts;
-//  * compute    4 waves in a 2 x 2 arrangement, each owning a
-//               (BM/2) x (BN/2) piece of C as independent 32x32 fp32
-//               accumulators, fed by v_mfma_f32_32x32x16_f16;
+//               written to a 2-stage LDS ring.  Buffer descriptors bound
+//               each operand tile, so rows past M / N read as zero;
+//  * LDS        a stage holds each operand as four 16-wide k planes of
+//               32-byte rows; within a row the two 16-byte halves swap by
+//               a bit of the row index and planes are padded, so both the
+//               MFMA fragment reads and the loader's writes are free of
+//               bank conflicts, and every LDS address is one per-lane base
+//               register plus an immediate offset;
+//  * compute    WM x WN waves, each owning a (BM/WM) x (BN/WN) piece of C
+//               as independent 32x32 fp32 accumulators fed by
+//               v_mfma_f32_32x32x16_f16; fragment reads run one 16-wide k
+//               step ahead of the MFMAs that use them;
 //  * epilogue   fp32 -> fp16 round-to-nearest-even, stores masked to
 //               [M, N].
 //
@@ -29,6 +31,8 @@
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
+
+#include <type_traits>
 
 #include "gemm_f16.h"
 #include "tile_sched.h"
@@ -40,9 +44,12 @@ typedef _Float16 half4 __attribute__((ext_vector_type(4)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef int int4v __attribute__((ext_vector_type(4)));
 
-constexpr int kThreads = 256;  // 4 waves of 64
 constexpr int kWave = 64;
 constexpr uint32_t kOutOfRange = 0x80000000u;  // buffer offset past any num_records: reads 0
+
+#ifndef GEMM_PLANE_PAD
+#define GEMM_PLANE_PAD 64
+#endif
 
 struct Params {
     const _Float16 *a;
@@ -56,13 +63,41 @@ struct Params {
     int32_t vec_c;         // C rows allow 8-byte stores (N % 4 == 0, c 8-byte aligned)
 };
 
-// Position of 16-byte chunk `c` of tile row `row` inside that row (8 chunks
-// per 128-byte row).  A 64-lane ds_read_b128 of a 32x32x16 MFMA fragment
-// reads 32 consecutive rows at one chunk; XORing with row ^ (row >> 3)
-// spreads any 8 consecutive rows over all 8 chunk slots and any 16
-// consecutive rows over distinct (row parity, slot) pairs, so neither
-// 8-lane nor 16-lane groups of the read hit a bank twice.
-__device__ __forceinline__ int swz8(int row) { return (row ^ (row >> 3)) & 7; }
+// Block-tile configuration: BM x BN output tile, K walked 64 at a time in
+// four 16-wide k steps, WM x WN waves each owning a (BM/WM) x (BN/WN) piece
+// of C made of 32x32 MFMA blocks.
+template <int BM_, int BN_, int WM_, int WN_>
+struct Cfg {
+    static constexpr int BM = BM_, BN = BN_, BK = 64, KS = 4;
+    static constexpr int WM = WM_, WN = WN_;
+    static constexpr int kWaves = WM * WN;
+    static constexpr int kThreads = kWaves * kWave;
+    static constexpr int TM = BM / WM, TN = BN / WN;
+    static constexpr int FM = TM / 32, FN = TN / 32;
+    static constexpr int kRowsPerPass = kThreads / 8;  // 8 chunks of 16 B per 64-wide row
+    static constexpr int kMinWavesPerEU = kWaves <= 4 ? 1 : kWaves / 4;
+    // LDS: per operand and stage, KS planes of ROWS x 32 B (+ padding).
+    static constexpr int kPlaneA = BM * 32 + GEMM_PLANE_PAD;
+    static constexpr int kPlaneB = BN * 32 + GEMM_PLANE_PAD;
+    static constexpr int kStageA = KS * kPlaneA;
+    static constexpr int kStageB = KS * kPlaneB;
+    static constexpr int kLdsB = 2 * kStageA;  // B's two stages follow A's
+    static constexpr int kLdsBytes = 2 * kStageA + 2 * kStageB;
+    static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be whole 32x32 blocks");
+    static_assert(kRowsPerPass % 32 == 0, "passes must keep row bits 2-4 per lane");
+    static_assert(BM % kRowsPerPass == 0 && BN % kRowsPerPass == 0, "loader passes");
+    static_assert(kStageA + (KS - 1) * kPlaneA + TM * 32 < 65536 &&
+                      kStageB + (KS - 1) * kPlaneB + TN * 32 < 65536,
+                  "LDS immediates must fit the 16-bit offset field");
+    static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
+};
+
+// Which 16-byte half of a 32-byte plane row holds k-half h of row `row`:
+// h ^ bit2(row) ^ bit3(row).  A fragment read touches 32 consecutive rows
+// at one half; with this swap any 16 consecutive rows land on 16 distinct
+// 16-byte bank groups (and any 8 on 8), and the loader's 8-lane row writes
+// spread over four planes whose padding shifts them to distinct groups.
+__device__ __forceinline__ int half_swap(int row) { return ((row >> 2) ^ (row >> 3)) & 1; }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
     // word3 0x00020000: raw (untyped) 32-bit data format, as gfx9-family
@@ -72,81 +107,86 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, ui
 }
 
 // LDS barrier that waits only for this wave's LDS traffic (lgkmcnt), not for
-// the global loads still in flight for the next K-tile.
+// the global loads still in flight for later K-tiles.
 __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-// One operand's K-tile: ROWS x 64 fp16, 8 chunks per row, 32 rows per
-// pass of the 256 threads; thread t owns chunk t % 8 of rows t / 8 + 32 i.
-template <int ROWS, bool VEC>
+// One operand's K-tile: ROWS x 64 fp16 = ROWS x 8 chunks of 16 bytes.  Each
+// pass of the workgroup covers RPP rows; thread t owns chunk t % 8 of rows
+// t / 8 + RPP * i, so every 8 consecutive lanes read one 128-byte row
+// segment.
+template <int ROWS, int RPP, bool VEC>
 struct TileLoader {
-    static constexpr int kPasses = ROWS / 32;
+    static constexpr int kPasses = ROWS / RPP;
     int4v regs[kPasses];
+    uint32_t voff[kPasses];  // VEC: byte offset of this lane's chunk from the K-tile start
+    int chunk, row0;
 
-    __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rsrc, int k_elems, int k0, int tid) {
-        const int chunk = tid & 7;
-        const int row0 = tid >> 3;
-        const int kc = k0 + chunk * 8;
+    __device__ __forceinline__ void init(int tid, int k_elems) {
+        chunk = tid & 7;
+        row0 = tid >> 3;
+#pragma unroll
+        for (int i = 0; i < kPasses; ++i) voff[i] = (uint32_t)((row0 + RPP * i) * k_elems + chunk * 8) * 2u;
+    }
+
+    // VEC: 0, or kOutOfRange when this lane's chunk of the K-tile starting
+    // at k0 lies past K (K % 8 == 0 on this path, so a chunk is wholly
+    // inside or wholly past K).  Computed once per K-tile.
+    __device__ __forceinline__ uint32_t k_mask(int k_elems, int k0) const {
+        return (k0 + chunk * 8 >= k_elems) ? kOutOfRange : 0u;
+    }
+
+    // VEC: rsrc_tile starts at this K-tile's first column and `mask` (from
+    // k_mask) pushes chunks past K out of range, so they read as zero.
+    // Scalar: every element is bounds-checked against K and the tile rows.
+    __device__ __forceinline__ void load(int i, __amdgpu_buffer_rsrc_t rsrc_tile, uint32_t mask,
+                                         __amdgpu_buffer_rsrc_t rsrc0, int k_elems, int k0) {
         if constexpr (VEC) {
-            // K % 8 == 0 here, so a chunk is either wholly inside K or wholly
-            // out.  Bit 31 is set when kc >= K (kc - K >= 0), which moves the
-            // offset past num_records; computed without a branch.
-            const uint32_t oor = (~(uint32_t)(kc - k_elems)) & kOutOfRange;
-#pragma unroll
-            for (int i = 0; i < kPasses; ++i) {
-                const int row = row0 + 32 * i;
-                const uint32_t off = ((uint32_t)(row * k_elems + kc) * 2u) | oor;
-                regs[i] = __builtin_amdgcn_raw_buffer_load_b128(rsrc, off, 0, 0);
-            }
+            regs[i] = __builtin_amdgcn_raw_buffer_load_b128(rsrc_tile, voff[i] | mask, 0, 0);
         } else {
+            const int row = row0 + RPP * i;
+            const int kc = k0 + chunk * 8;
+            union {
+                short s[8];
+                int4v v;
+            } u;
 #pragma unroll
-            for (int i = 0; i < kPasses; ++i) {
-                const int row = row0 + 32 * i;
-                union {
-                    short s[8];
-                    int4v v;
-                } u;
-#pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const uint32_t off =
-                        (kc + e < k_elems) ? (uint32_t)(row * k_elems + kc + e) * 2u : kOutOfRange;
-                    u.s[e] = __builtin_amdgcn_raw_buffer_load_b16(rsrc, off, 0, 0);
-                }
-                regs[i] = u.v;
+            for (int e = 0; e < 8; ++e) {
+                const uint32_t off =
+                    (kc + e < k_elems) ? (uint32_t)(row * k_elems + kc + e) * 2u : kOutOfRange;
+                u.s[e] = __builtin_amdgcn_raw_buffer_load_b16(rsrc0, off, 0, 0);
             }
+            regs[i] = u.v;
         }
     }
 
-    __device__ __forceinline__ void store(int4v *lds_tile, int tid) const {
-        const int chunk = tid & 7;
-        const int row0 = tid >> 3;
-#pragma unroll
-        for (int i = 0; i < kPasses; ++i) {
-            const int row = row0 + 32 * i;
-            lds_tile[row * 8 + (chunk ^ swz8(row))] = regs[i];
-        }
+    // LDS byte offset of this lane's chunk in pass 0 (plane = chunk / 2).
+    template <int PLANE>
+    __device__ __forceinline__ int lds_lane_offset() const {
+        return (chunk >> 1) * PLANE + row0 * 32 + (((chunk & 1) ^ half_swap(row0)) * 16);
     }
 };
 
-template <int BM, int BN, bool VEC>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(1, 1)))
+template <class C, bool VEC>
+__global__ __launch_bounds__(C::kThreads)
+__attribute__((amdgpu_waves_per_eu(C::kMinWavesPerEU, C::kMinWavesPerEU)))
 void gemm_f16_nt_kernel(const Params p) {
-    constexpr int BK = 64;
-    constexpr int TM = BM / 2;  // wave tile (2 x 2 waves)
-    constexpr int TN = BN / 2;
-    constexpr int FM = TM / 32;  // 32x32 MFMA blocks per wave
-    constexpr int FN = TN / 32;
-    constexpr int kStageChunks = (BM + BN) * (BK / 8);
-    __shared__ int4v smem[2 * kStageChunks];
+    constexpr int BM = C::BM, BN = C::BN, BK = C::BK, KS = C::KS;
+    constexpr int TM = C::TM, TN = C::TN, FM = C::FM, FN = C::FN;
+    constexpr int RPP = C::kRowsPerPass;
+    using LoaderA = TileLoader<BM, RPP, VEC>;
+    using LoaderB = TileLoader<BN, RPP, VEC>;
+    constexpr int PA = LoaderA::kPasses, PB = LoaderB::kPasses;
+    __shared__ __attribute__((aligned(1024))) char smem[C::kLdsBytes];
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wave = tid / kWave;
-    const int wm = wave >> 1;
-    const int wn = wave & 1;
+    const int wm = wave / C::WN;
+    const int wn = wave % C::WN;
 
     const TileCoord tc = tile_coord(blockIdx.x, p.num_m, p.num_n, p.swizzle, p.xcd != 0);
     const int m0 = (int)tc.m_block * BM;
@@ -155,75 +195,172 @@ void gemm_f16_nt_kernel(const Params p) {
     // Per-tile buffer descriptors: rows past M (N) lie beyond num_records.
     const int rows_a = min(BM, p.m - m0);
     const int rows_b = min(BN, p.n - n0);
-    const __amdgpu_buffer_rsrc_t ra =
-        make_rsrc(p.a + (int64_t)m0 * p.k, (uint32_t)rows_a * (uint32_t)p.k * 2u);
-    const __amdgpu_buffer_rsrc_t rb =
-        make_rsrc(p.b + (int64_t)n0 * p.k, (uint32_t)rows_b * (uint32_t)p.k * 2u);
+    const _Float16 *a_tile = p.a + (int64_t)m0 * p.k;
+    const _Float16 *b_tile = p.b + (int64_t)n0 * p.k;
+    const uint32_t bytes_a = (uint32_t)rows_a * (uint32_t)p.k * 2u;
+    const uint32_t bytes_b = (uint32_t)rows_b * (uint32_t)p.k * 2u;
+    const __amdgpu_buffer_rsrc_t ra0 = make_rsrc(a_tile, bytes_a);
+    const __amdgpu_buffer_rsrc_t rb0 = make_rsrc(b_tile, bytes_b);
+    // Descriptor of K-tile t: starts t*BK columns in and its range shrinks
+    // to match; a K-tile at or past K (fetched by the last iterations, never
+    // used) gets an empty range, so nothing is read.
+    auto rsrc_at = [&](const _Float16 *tile, uint32_t bytes, int t) {
+        const uint32_t skip = (uint32_t)t * (BK * 2);
+        return make_rsrc(tile + (t < p.k_tiles ? t * BK : 0), (t < p.k_tiles && bytes > skip) ? bytes - skip : 0u);
+    };
 
-    TileLoader<BM, VEC> la;
-    TileLoader<BN, VEC> lb;
+    LoaderA la;
+    LoaderB lb;
+    la.init(tid, p.k);
+    lb.init(tid, p.k);
+    const int wa_lane = la.template lds_lane_offset<C::kPlaneA>();
+    const int wb_lane = C::kLdsB + lb.template lds_lane_offset<C::kPlaneB>();
 
     floatx16 acc[FN][FM];
 #pragma unroll
-    for (int i = 0; i < FN; ++i)
+    for (int j = 0; j < FN; ++j)
 #pragma unroll
-        for (int j = 0; j < FM; ++j) acc[i][j] = floatx16{};
+        for (int i = 0; i < FM; ++i) acc[j][i] = floatx16{};
+
+    // Fragment reads: lane l reads row (wave tile row) + l % 32 at k half
+    // l / 32 of each 16-wide k step.
+    const int frow = lane & 31;
+    const int fhalf = lane >> 5;
+    const int ra_lane = (wm * TM + frow) * 32 + ((fhalf ^ half_swap(frow)) * 16);
+    const int rb_lane = C::kLdsB + (wn * TN + frow) * 32 + ((fhalf ^ half_swap(frow)) * 16);
+    half8 af[2][FM];
+    half8 bf[2][FN];
+    auto read_frags = [&](int buf, int stage, int ks) {
+        // in the order the MFMAs consume them: B0, A0..A(FM-1), B1..
+        bf[buf][0] = *reinterpret_cast<const half8 *>(smem + rb_lane + stage * C::kStageB + ks * C::kPlaneB);
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+            af[buf][i] = *reinterpret_cast<const half8 *>(smem + ra_lane + stage * C::kStageA +
+                                                          ks * C::kPlaneA + i * 1024);
+#pragma unroll
+        for (int j = 1; j < FN; ++j)
+            bf[buf][j] = *reinterpret_cast<const half8 *>(smem + rb_lane + stage * C::kStageB +
+                                                          ks * C::kPlaneB + j * 1024);
+    };
+    auto store_a = [&](int i, int stage) {
+        *reinterpret_cast<int4v *>(smem + wa_lane + stage * C::kStageA + i * RPP * 32) = la.regs[i];
+    };
+    auto store_b = [&](int i, int stage) {
+        *reinterpret_cast<int4v *>(smem + wb_lane + stage * C::kStageB + i * RPP * 32) = lb.regs[i];
+    };
 
     const int kt_count = p.k_tiles;
-    if (kt_count > 0) {
-        la.load(ra, p.k, 0, tid);
-        lb.load(rb, p.k, 0, tid);
-        la.store(smem, tid);
-        lb.store(smem + BM * 8, tid);
-        if (kt_count > 1) {
-            la.load(ra, p.k, BK, tid);
-            lb.load(rb, p.k, BK, tid);
-        }
-        lds_barrier();
+    if (kt_count == 0) return;  // never launched with K == 0
+
+    // Prologue: K-tile 0 into stage 0, K-tile 1 (zeros if K has one K-tile)
+    // into the staging registers.
+    {
+        const __amdgpu_buffer_rsrc_t a_t = rsrc_at(a_tile, bytes_a, 0), b_t = rsrc_at(b_tile, bytes_b, 0);
+        const uint32_t ma = la.k_mask(p.k, 0), mb = lb.k_mask(p.k, 0);
+#pragma unroll
+        for (int i = 0; i < PA; ++i) la.load(i, a_t, ma, ra0, p.k, 0);
+#pragma unroll
+        for (int i = 0; i < PB; ++i) lb.load(i, b_t, mb, rb0, p.k, 0);
+#pragma unroll
+        for (int i = 0; i < PA; ++i) store_a(i, 0);
+#pragma unroll
+        for (int i = 0; i < PB; ++i) store_b(i, 0);
     }
-
-    // Fragment rows this lane reads: lanes 0-31 and 32-63 take the two
-    // 8-wide k halves of each 16-wide k step.
-    const int frag_row = lane & 31;
-    const int frag_half = lane >> 5;
-
-    for (int kt = 0; kt < kt_count; ++kt) {
-        const int4v *sa = smem + (kt & 1) * kStageChunks;
-        const int4v *sb = sa + BM * 8;
+    {
+        const __amdgpu_buffer_rsrc_t a_t = rsrc_at(a_tile, bytes_a, 1), b_t = rsrc_at(b_tile, bytes_b, 1);
+        const uint32_t ma = la.k_mask(p.k, BK), mb = lb.k_mask(p.k, BK);
 #pragma unroll
-        for (int ks = 0; ks < BK / 16; ++ks) {
-            const int chunk = ks * 2 + frag_half;
-            half8 af[FM];
-            half8 bf[FN];
+        for (int i = 0; i < PA; ++i) la.load(i, a_t, ma, ra0, p.k, BK);
 #pragma unroll
-            for (int i = 0; i < FM; ++i) {
-                const int row = wm * TM + i * 32 + frag_row;
-                af[i] = __builtin_bit_cast(half8, sa[row * 8 + (chunk ^ swz8(row))]);
+        for (int i = 0; i < PB; ++i) lb.load(i, b_t, mb, rb0, p.k, BK);
+    }
+    lds_barrier();
+    read_frags(0, 0, 0);
+
+    // One K-tile of work, as KS 16-wide k steps on stage STAGE, which also
+    // moves the staged K-tile kt+1 into the other stage and refills the
+    // staging registers with K-tile kt+2.  Past the last K-tile those moves
+    // carry zeros that are never read, so every iteration is the same
+    // branch-free block, whose issue order is pinned:
+    //   step ks < KS-1: MFMAs of step ks interleaved with the fragment reads
+    //                   for step ks+1 and a slice of the LDS writes and
+    //                   global loads;
+    //   step KS-1:      wait for this wave's LDS traffic, workgroup barrier,
+    //                   then MFMAs of step KS-1 interleaved with the
+    //                   fragment reads for step 0 of K-tile kt+1.
+    constexpr int kSlices = KS - 1;
+    auto k_iter = [&](auto stage_tag, int kt) {
+        constexpr int STAGE = decltype(stage_tag)::value;
+        constexpr int NXT = STAGE ^ 1;
+        const int k_load = (kt + 2) * BK;
+        const __amdgpu_buffer_rsrc_t a_t = rsrc_at(a_tile, bytes_a, kt + 2);
+        const __amdgpu_buffer_rsrc_t b_t = rsrc_at(b_tile, bytes_b, kt + 2);
+        const uint32_t ma = la.k_mask(p.k, k_load), mb = lb.k_mask(p.k, k_load);
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) {
+            const int cur = ks & 1;
+            constexpr int NM = FM * FN;
+            if (ks + 1 < KS) {
+                read_frags(cur ^ 1, STAGE, ks + 1);
+            } else {
+                // The other stage is complete for everyone, and everyone has
+                // read its last fragments of this stage.
+                lds_barrier();
+                read_frags(cur ^ 1, NXT, 0);
             }
+            if (ks < kSlices) {
 #pragma unroll
-            for (int j = 0; j < FN; ++j) {
-                const int row = wn * TN + j * 32 + frag_row;
-                bf[j] = __builtin_bit_cast(half8, sb[row * 8 + (chunk ^ swz8(row))]);
+                for (int i = ks * PA / kSlices; i < (ks + 1) * PA / kSlices; ++i) {
+                    store_a(i, NXT);
+                    la.load(i, a_t, ma, ra0, p.k, k_load);
+                }
+#pragma unroll
+                for (int i = ks * PB / kSlices; i < (ks + 1) * PB / kSlices; ++i) {
+                    store_b(i, NXT);
+                    lb.load(i, b_t, mb, rb0, p.k, k_load);
+                }
             }
             // B rows feed the MFMA's A operand and A rows its B operand, so
-            // the 32x32 result block is C^T: each lane then holds 4
+            // each 32x32 result block is C^T: a lane then holds 4
             // consecutive n of one m row, which stores as 8 bytes.
 #pragma unroll
             for (int j = 0; j < FN; ++j)
 #pragma unroll
                 for (int i = 0; i < FM; ++i)
-                    acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf[j], af[i], acc[j][i], 0, 0, 0);
-        }
-        if (kt + 1 < kt_count) {
-            int4v *nxt = smem + ((kt + 1) & 1) * kStageChunks;
-            la.store(nxt, tid);
-            lb.store(nxt + BM * 8, tid);
-            if (kt + 2 < kt_count) {
-                la.load(ra, p.k, (kt + 2) * BK, tid);
-                lb.load(rb, p.k, (kt + 2) * BK, tid);
+                    acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf[cur][j], af[cur][i], acc[j][i],
+                                                                      0, 0, 0);
+            // Pin the issue order: after each MFMA, an even share of this
+            // step's other memory instructions (fragment reads first, then
+            // LDS write / global load pairs).
+            {
+                const int nr = FM + FN;
+                const int nw = ks < kSlices ? ((ks + 1) * PA / kSlices - ks * PA / kSlices) +
+                                                  ((ks + 1) * PB / kSlices - ks * PB / kSlices)
+                                            : 0;
+                const int total = nr + 2 * nw;
+#pragma unroll
+                for (int m = 0; m < NM; ++m) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+#pragma unroll
+                    for (int o = m * total / NM; o < (m + 1) * total / NM; ++o) {
+                        if (o < nr) {
+                            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
+                        } else if (((o - nr) & 1) == 0) {
+                            __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // DS write
+                        } else {
+                            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read
+                        }
+                    }
+                }
             }
+            __builtin_amdgcn_sched_barrier(0);
         }
-        lds_barrier();
+    };
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
+    for (int kt = 0; kt < kt_count; kt += 2) {
+        k_iter(S0{}, kt);
+        if (kt + 1 < kt_count) k_iter(S1{}, kt + 1);
     }
 
     // Epilogue.  32x32 MFMA result layout: lane l, register r holds row
@@ -232,7 +369,7 @@ void gemm_f16_nt_kernel(const Params p) {
     const int quad = (lane >> 5) * 4;
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
-        const int m = m0 + wm * TM + i * 32 + frag_row;
+        const int m = m0 + wm * TM + i * 32 + frow;
         if (m >= p.m) continue;
         _Float16 *crow = p.c + (int64_t)m * p.n;
 #pragma unroll
@@ -265,6 +402,13 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(_Float16 *c, int64_t cou
 }
 
 // ---- host side --------------------------------------------------------------
+
+#ifndef GEMM_CFG256
+#define GEMM_CFG256 256, 256, 2, 4
+#endif
+using Cfg256 = Cfg<GEMM_CFG256>;
+using Cfg128 = Cfg<128, 128, 2, 2>;
+using Cfg64 = Cfg<64, 64, 2, 2>;
 
 struct TileShape {
     int bm, bn;
@@ -318,13 +462,13 @@ static int check_device() {
     return cached[dev] == 1 ? GEMM_F16_OK : GEMM_F16_EDEVICE;
 }
 
-template <int BM, int BN>
+template <class C>
 static void launch(const Params &p, bool vec, hipStream_t stream) {
     const dim3 grid((unsigned)((int64_t)p.num_m * p.num_n));
     if (vec)
-        hipLaunchKernelGGL((gemm_f16_nt_kernel<BM, BN, true>), grid, dim3(kThreads), 0, stream, p);
+        hipLaunchKernelGGL((gemm_f16_nt_kernel<C, true>), grid, dim3(C::kThreads), 0, stream, p);
     else
-        hipLaunchKernelGGL((gemm_f16_nt_kernel<BM, BN, false>), grid, dim3(kThreads), 0, stream, p);
+        hipLaunchKernelGGL((gemm_f16_nt_kernel<C, false>), grid, dim3(C::kThreads), 0, stream, p);
 }
 
 }  // namespace gemm_f16
@@ -393,9 +537,9 @@ int gemm_f16_nt_ex(int64_t m, int64_t n, int64_t k, const void *a, const void *b
     if ((int64_t)p.num_m * p.num_n >= (int64_t(1) << 31)) return GEMM_F16_EINVAL;
 
     switch (tile) {
-        case GEMM_F16_TILE_256x256: launch<256, 256>(p, vec, s); break;
-        case GEMM_F16_TILE_128x128: launch<128, 128>(p, vec, s); break;
-        default: launch<64, 64>(p, vec, s); break;
+        case GEMM_F16_TILE_256x256: launch<Cfg256>(p, vec, s); break;
+        case GEMM_F16_TILE_128x128: launch<Cfg128>(p, vec, s); break;
+        default: launch<Cfg64>(p, vec, s); break;
     }
     return hipGetLastError() == hipSuccess ? GEMM_F16_OK : GEMM_F16_EHIP;
 }
