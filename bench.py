@@ -18,7 +18,6 @@ the same rows double as a parity spot check of the timed output.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import sys
@@ -29,16 +28,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "fp16 GEMM TFLOP/s (fp32 acc) at 8192³; % of MI355X dense fp16 MFMA peak"
 PEAK_TFLOPS = 2500.0  # MI355X dense fp16 MFMA, published
-KERNEL_SRC = os.path.join(ROOT, "dense_fp16_gemm_f16_amd", "csrc", "gemm_f16.hip")
 PROFILE_DIR = os.path.join(ROOT, "profiles")
-
-
-def kernel_source_hash() -> str:
-    h = hashlib.sha256()
-    for name in ("gemm_f16.hip", "tile_sched.h"):
-        with open(os.path.join(os.path.dirname(KERNEL_SRC), name), "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()[:16]
 
 
 def measured_traffic(workload: str):
@@ -49,6 +39,8 @@ def measured_traffic(workload: str):
         return None
     with open(path) as f:
         rec = json.load(f)
+    from dense_fp16_gemm_f16_amd.profile_summary import kernel_source_hash
+
     if rec.get("kernel_source_sha256_16") != kernel_source_hash():
         return None
     return rec.get("hbm_bytes_per_launch")
@@ -62,11 +54,11 @@ def cpu_baseline(a, b, c_gpu, w, budget_s: float):
 
     threads = oracle.default_threads()
     rng = np.random.default_rng(12345)
-    # calibrate on one row, then size the sample to the time budget
+    # calibrate on one row per thread, then size the sample to the time budget
     t0 = time.perf_counter()
-    first = oracle.gemm_f16_nt_rows(a, b, [0], threads)
-    t_one = max(time.perf_counter() - t0, 1e-6)
-    rows_fit = int(budget_s / t_one)
+    first = oracle.gemm_f16_nt_rows(a, b, list(range(min(threads, w.m))), threads)
+    t_round = max(time.perf_counter() - t0, 1e-6)  # one row on every thread
+    rows_fit = int(budget_s / t_round) * threads
     nrows = max(threads, min(w.m, (rows_fit // threads) * threads or threads))
     rows = np.sort(rng.choice(w.m, size=min(nrows, w.m), replace=False))
     t0 = time.perf_counter()
@@ -108,6 +100,9 @@ def main() -> int:
     ap.add_argument("--xcd", type=int, default=-1)
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle work for the CPU baseline (0 = skip)")
+    ap.add_argument("--traffic-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run a plain elementwise copy (negation) of BYTES, 3 times: the "
+                         "reference for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -117,6 +112,16 @@ def main() -> int:
 
     import numpy as np
     import torch
+
+    if args.traffic_calibration:
+        n = args.traffic_calibration // 4
+        src = torch.ones(n, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)  # one elementwise kernel: reads and writes BYTES
+        torch.cuda.synchronize()
+        print(json.dumps({"traffic_calibration_bytes": n * 4}), flush=True)
+        return 0
 
     import dense_fp16_gemm_f16_amd as g
     from dense_fp16_gemm_f16_amd import inputs

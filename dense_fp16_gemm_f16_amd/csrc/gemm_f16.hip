@@ -48,7 +48,7 @@ constexpr int kWave = 64;
 constexpr uint32_t kOutOfRange = 0x80000000u;  // buffer offset past any num_records: reads 0
 
 #ifndef GEMM_PLANE_PAD
-#define GEMM_PLANE_PAD 64
+#define GEMM_PLANE_PAD 32
 #endif
 
 struct Params {
@@ -94,9 +94,11 @@ struct Cfg {
 
 // Which 16-byte half of a 32-byte plane row holds k-half h of row `row`:
 // h ^ bit2(row) ^ bit3(row).  A fragment read touches 32 consecutive rows
-// at one half; with this swap any 16 consecutive rows land on 16 distinct
-// 16-byte bank groups (and any 8 on 8), and the loader's 8-lane row writes
-// spread over four planes whose padding shifts them to distinct groups.
+// at one half; with this swap its ds_read_b128 is free of bank conflicts.
+// The loader's 8-lane groups write one row's four planes; a 32-byte plane
+// padding staggers those planes across banks so its ds_write_b128 is free
+// of conflicts too (64 bytes, or none, costs 8-24 conflict cycles per
+// write on gfx950, measured with SQ_LDS_BANK_CONFLICT).
 __device__ __forceinline__ int half_swap(int row) { return ((row >> 2) ^ (row >> 3)) & 1; }
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
@@ -404,7 +406,7 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(_Float16 *c, int64_t cou
 // ---- host side --------------------------------------------------------------
 
 #ifndef GEMM_CFG256
-#define GEMM_CFG256 256, 256, 2, 4
+#define GEMM_CFG256 256, 256, 4, 2
 #endif
 using Cfg256 = Cfg<GEMM_CFG256>;
 using Cfg128 = Cfg<128, 128, 2, 2>;

@@ -1,0 +1,110 @@
+"""Summaries of rocprofv3 CSV output for the GEMM kernel.
+
+    python -m dense_fp16_gemm_f16_amd.profile_summary stats DIR [--kernel gemm_f16_nt_kernel]
+    python -m dense_fp16_gemm_f16_amd.profile_summary traffic \\
+        --gemm-fetch DIR --gemm-write DIR --copy-fetch DIR --copy-write DIR \\
+        --copy-bytes N --workload NAME --out profiles/traffic_NAME.json
+
+`stats` reads <DIR>/*_kernel_stats.csv (rocprofv3 --kernel-trace --stats
+--output-format csv).  `traffic` reads <DIR>/*_counter_collection.csv of
+--pmc FETCH_SIZE / --pmc WRITE_SIZE runs (values in KiB per dispatch), scales
+each by the ratio of a plain copy's known bytes to what the same counter
+reported for it, and writes HBM bytes per GEMM launch together with a hash
+of the kernel source, so that stale counters are never reported for a
+changed kernel.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import glob
+import hashlib
+import json
+import os
+import statistics
+import sys
+
+CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for name in ("gemm_f16.hip", "tile_sched.h"):
+        with open(os.path.join(CSRC, name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def _one(pattern: str) -> str:
+    files = sorted(glob.glob(pattern, recursive=True))
+    if not files:
+        raise FileNotFoundError(pattern)
+    return files[0]
+
+
+def kernel_stats(d: str, kernel: str) -> dict:
+    path = _one(os.path.join(d, "**", "*kernel_stats.csv"))
+    for r in csv.DictReader(open(path)):
+        if kernel in r["Name"]:
+            return {"name": r["Name"], "calls": int(r["Calls"]), "avg_us": float(r["AverageNs"]) / 1e3,
+                    "min_us": float(r["MinNs"]) / 1e3, "max_us": float(r["MaxNs"]) / 1e3}
+    raise KeyError(kernel)
+
+
+def counter_per_dispatch(d: str, kernel: str, counter: str) -> list[float]:
+    path = _one(os.path.join(d, "**", "*counter_collection.csv"))
+    per = {}
+    for r in csv.DictReader(open(path)):
+        if kernel in r["Kernel_Name"] and r["Counter_Name"] == counter:
+            per[int(r["Dispatch_Id"])] = per.get(int(r["Dispatch_Id"]), 0.0) + float(r["Counter_Value"])
+    return [per[k] for k in sorted(per)]
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    s1 = sub.add_parser("stats")
+    s1.add_argument("dir")
+    s1.add_argument("--kernel", default="gemm_f16_nt_kernel")
+    s2 = sub.add_parser("traffic")
+    for k in ("gemm-fetch", "gemm-write", "copy-fetch", "copy-write", "workload", "out"):
+        s2.add_argument("--" + k, required=True)
+    s2.add_argument("--copy-bytes", type=int, required=True)
+    s2.add_argument("--kernel", default="gemm_f16_nt_kernel")
+    s2.add_argument("--copy-kernel", default="copy")
+    s2.add_argument("--command", default="")
+    a = ap.parse_args(argv)
+    if a.cmd == "stats":
+        print(json.dumps(kernel_stats(a.dir, a.kernel)))
+        return 0
+    fetch = counter_per_dispatch(a.gemm_fetch, a.kernel, "FETCH_SIZE")
+    write = counter_per_dispatch(a.gemm_write, a.kernel, "WRITE_SIZE")
+    cf = counter_per_dispatch(a.copy_fetch, a.copy_kernel, "FETCH_SIZE")
+    cw = counter_per_dispatch(a.copy_write, a.copy_kernel, "WRITE_SIZE")
+    f_scale = a.copy_bytes / (statistics.median(cf) * 1024.0)
+    w_scale = a.copy_bytes / (statistics.median(cw) * 1024.0)
+    fetch_b = statistics.median(fetch) * 1024.0 * f_scale
+    write_b = statistics.median(write) * 1024.0 * w_scale
+    rec = {
+        "workload": a.workload,
+        "kernel_source_sha256_16": kernel_source_hash(),
+        "fetch_kib_per_dispatch": fetch,
+        "write_kib_per_dispatch": write,
+        "copy_bytes": a.copy_bytes,
+        "copy_fetch_kib": cf,
+        "copy_write_kib": cw,
+        "fetch_scale": f_scale,
+        "write_scale": w_scale,
+        "hbm_fetch_bytes_per_launch": fetch_b,
+        "hbm_write_bytes_per_launch": write_b,
+        "hbm_bytes_per_launch": fetch_b + write_b,
+        "command": a.command,
+    }
+    with open(a.out, "w") as f:
+        json.dump(rec, f, indent=1)
+    print(json.dumps(rec))
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())
