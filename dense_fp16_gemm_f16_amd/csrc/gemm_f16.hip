@@ -18,7 +18,7 @@
 //               MFMA fragment reads and the loader's writes are free of
 //               bank conflicts, and every LDS address is one per-lane base
 //               register plus an immediate offset;
-//  * compute    WM x WN waves, each owning a (BM/WM) x (BN/WN) piece of C
+//  * compute    WM x WN waves (4 or 8), each owning a (BM/WM) x (BN/WN) piece of C
 //               as independent 32x32 fp32 accumulators fed by
 //               v_mfma_f32_32x32x16_f16; fragment reads run one 16-wide k
 //               step ahead of the MFMAs that use them;
@@ -360,9 +360,13 @@ void gemm_f16_nt_kernel(const Params p) {
     };
     using S0 = std::integral_constant<int, 0>;
     using S1 = std::integral_constant<int, 1>;
+    // K-tiles go in pairs (stage 0, stage 1) with no branch between them.
+    // When the count is odd the last pair's second K-tile lies past K: its
+    // stage holds zeros, so its MFMAs add +0 to accumulators that are never
+    // -0 (they start at +0), which leaves every bit unchanged.
     for (int kt = 0; kt < kt_count; kt += 2) {
         k_iter(S0{}, kt);
-        if (kt + 1 < kt_count) k_iter(S1{}, kt + 1);
+        k_iter(S1{}, kt + 1);
     }
 
     // Epilogue.  32x32 MFMA result layout: lane l, register r holds row
@@ -405,10 +409,10 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(_Float16 *c, int64_t cou
 
 // ---- host side --------------------------------------------------------------
 
-#ifndef GEMM_CFG256
-#define GEMM_CFG256 256, 256, 4, 2
-#endif
-using Cfg256 = Cfg<GEMM_CFG256>;
+using Cfg256 = Cfg<256, 256, 2, 2>;   // 4 waves, 128x128 each
+using Cfg256w8 = Cfg<256, 256, 4, 2>; // 8 waves, 64x128 each
+using Cfg256x128 = Cfg<256, 128, 2, 2>;
+using Cfg128x256 = Cfg<128, 256, 2, 2>;
 using Cfg128 = Cfg<128, 128, 2, 2>;
 using Cfg64 = Cfg<64, 64, 2, 2>;
 
@@ -419,6 +423,9 @@ struct TileShape {
 static TileShape tile_shape(int tile) {
     switch (tile) {
         case GEMM_F16_TILE_256x256: return {256, 256};
+        case GEMM_F16_TILE_256x256_W8: return {256, 256};
+        case GEMM_F16_TILE_256x128: return {256, 128};
+        case GEMM_F16_TILE_128x256: return {128, 256};
         case GEMM_F16_TILE_128x128: return {128, 128};
         default: return {64, 64};
     }
@@ -426,12 +433,38 @@ static TileShape tile_shape(int tile) {
 
 static int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Largest tile that still gives at least one workgroup per CU (256 CUs);
-// otherwise the tile with the most workgroups.
+constexpr int kNumCU = 256;
+
+// Automatic block tile: the candidate with the best modelled throughput,
+// (work per launch) / (rounds of 256 workgroups x per-tile efficiency).  A
+// round is one workgroup per CU; the efficiency factors are relative
+// per-CU throughputs of the tile shapes measured on MI355X (the bigger the
+// tile, the fewer LDS and L2 bytes per flop).
 static int auto_tile(int64_t m, int64_t n) {
-    if (cdiv(m, 256) * cdiv(n, 256) >= 256) return GEMM_F16_TILE_256x256;
-    if (cdiv(m, 128) * cdiv(n, 128) >= 128) return GEMM_F16_TILE_128x128;
-    return GEMM_F16_TILE_64x64;
+    struct Cand {
+        int id, bm, bn;
+        double eff;
+    };
+    static const Cand cands[] = {
+        {GEMM_F16_TILE_256x256, 256, 256, 1.00},
+        {GEMM_F16_TILE_256x128, 256, 128, 0.90},
+        {GEMM_F16_TILE_128x256, 128, 256, 0.90},
+        {GEMM_F16_TILE_128x128, 128, 128, 0.75},
+        {GEMM_F16_TILE_64x64, 64, 64, 0.35},
+    };
+    int best = GEMM_F16_TILE_64x64;
+    double best_t = 1e300;
+    for (const Cand &c : cands) {
+        const int64_t tiles = cdiv(m, c.bm) * cdiv(n, c.bn);
+        const int64_t rounds = cdiv(tiles, kNumCU);
+        // time ~ rounds * (tile flops) / eff; tile flops ~ bm * bn
+        const double t = (double)rounds * c.bm * c.bn / c.eff;
+        if (t < best_t * 0.999) {
+            best_t = t;
+            best = c.id;
+        }
+    }
+    return best;
 }
 
 static int check_sizes(int64_t m, int64_t n, int64_t k) {
@@ -502,7 +535,7 @@ int gemm_f16_nt_ex(int64_t m, int64_t n, int64_t k, const void *a, const void *b
     if (rc != GEMM_F16_OK) return rc;
     gemm_f16_options o = {0, 0, -1, 0};
     if (opt) o = *opt;
-    if (o.tile < 0 || o.tile > GEMM_F16_TILE_64x64 || o.swizzle < 0 || o.xcd < -1 || o.xcd > 1)
+    if (o.tile < 0 || o.tile > GEMM_F16_TILE_LAST || o.swizzle < 0 || o.xcd < -1 || o.xcd > 1)
         return GEMM_F16_EINVAL;
     if (m == 0 || n == 0) return GEMM_F16_OK;
     if (!c || (k > 0 && (!a || !b))) return GEMM_F16_ENULL;
@@ -540,6 +573,9 @@ int gemm_f16_nt_ex(int64_t m, int64_t n, int64_t k, const void *a, const void *b
 
     switch (tile) {
         case GEMM_F16_TILE_256x256: launch<Cfg256>(p, vec, s); break;
+        case GEMM_F16_TILE_256x256_W8: launch<Cfg256w8>(p, vec, s); break;
+        case GEMM_F16_TILE_256x128: launch<Cfg256x128>(p, vec, s); break;
+        case GEMM_F16_TILE_128x256: launch<Cfg128x256>(p, vec, s); break;
         case GEMM_F16_TILE_128x128: launch<Cfg128>(p, vec, s); break;
         default: launch<Cfg64>(p, vec, s); break;
     }

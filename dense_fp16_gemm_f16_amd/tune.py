@@ -1,0 +1,76 @@
+"""Offline sweep of block tile and rasterization options on one GPU.
+
+    python -m dense_fp16_gemm_f16_amd.tune [--shapes M,N,K ...] [--rounds 3]
+
+For every shape (default: the five benchmark workloads) it times each block
+tile (and, for the default tile, a few swizzle widths) with HIP events,
+interleaving the candidates over several rounds and taking the median, on
+uniform[-1,1] fp16 operands.  One JSON line per (shape, option), then one
+line per shape naming the fastest option.  The automatic tile choice in the
+library (gemm_f16_select_tile) is meant to agree with these results.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import statistics
+import sys
+
+import dense_fp16_gemm_f16_amd as g
+from dense_fp16_gemm_f16_amd import inputs
+
+
+def main(argv=None) -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--shapes", nargs="*", default=None, help="M,N,K triples")
+    ap.add_argument("--rounds", type=int, default=3)
+    ap.add_argument("--reps", type=int, default=10)
+    ap.add_argument("--swizzles", default="1,4,8")
+    a = ap.parse_args(argv)
+    import torch
+
+    shapes = ([tuple(int(x) for x in s.split(",")) for s in a.shapes] if a.shapes else
+              [(w.m, w.n, w.k) for w in inputs.WORKLOADS.values()])
+    swz = [int(x) for x in a.swizzles.split(",")]
+    gen = torch.Generator(device="cuda").manual_seed(0)
+    stream = torch.cuda.current_stream()
+    for (m, n, k) in shapes:
+        A = (torch.rand((m, k), device="cuda", generator=gen) * 2 - 1).half()
+        B = (torch.rand((n, k), device="cuda", generator=gen) * 2 - 1).half()
+        C = torch.empty((m, n), device="cuda", dtype=torch.float16)
+        auto = g.select_tile(m, n, k)
+        opts = [(t, 0, -1) for t in sorted(g.TILES)] + [(auto, s, x) for s in swz for x in (0, 1)]
+        times = {o: [] for o in opts}
+        for _ in range(a.rounds):
+            for o in opts:
+                def run():
+                    rc = g.gemm_f16_nt_raw(m, n, k, A.data_ptr(), B.data_ptr(), C.data_ptr(),
+                                           stream.cuda_stream, *o)
+                    if rc != g.OK:
+                        raise g.GemmError(rc)
+                for _ in range(2):
+                    run()
+                ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                      for _ in range(a.reps)]
+                for e0, e1 in ev:
+                    e0.record(stream)
+                    run()
+                    e1.record(stream)
+                torch.cuda.synchronize()
+                times[o].append(statistics.median(e0.elapsed_time(e1) for e0, e1 in ev))
+        best = None
+        for o in opts:
+            us = statistics.median(times[o]) * 1e3
+            tf = 2.0 * m * n * k / (us * 1e-6) / 1e12
+            print(json.dumps({"shape": [m, n, k], "tile": o[0], "swizzle": o[1], "xcd": o[2],
+                              "us": round(us, 2), "tflops": round(tf, 1), "auto": o[0] == auto}), flush=True)
+            if best is None or us < best[1]:
+                best = (o, us)
+        print(json.dumps({"shape": [m, n, k], "best": best[0], "best_us": round(best[1], 2),
+                          "auto_tile": auto}), flush=True)
+        del A, B, C
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

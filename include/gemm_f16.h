@@ -85,9 +85,13 @@ typedef struct {
 
 enum {
     GEMM_F16_TILE_AUTO = 0,
-    GEMM_F16_TILE_256x256 = 1,  /* 4 waves, each 128x128 of C */
-    GEMM_F16_TILE_128x128 = 2,  /* 4 waves, each 64x64 of C */
-    GEMM_F16_TILE_64x64 = 3     /* 4 waves, each 32x32 of C */
+    GEMM_F16_TILE_256x256 = 1,     /* 4 waves, each 128x128 of C */
+    GEMM_F16_TILE_128x128 = 2,     /* 4 waves, each 64x64 of C */
+    GEMM_F16_TILE_64x64 = 3,       /* 4 waves, each 32x32 of C */
+    GEMM_F16_TILE_256x256_W8 = 4,  /* 8 waves, each 64x128 of C */
+    GEMM_F16_TILE_256x128 = 5,     /* 4 waves, each 128x64 of C */
+    GEMM_F16_TILE_128x256 = 6,     /* 4 waves, each 64x128 of C */
+    GEMM_F16_TILE_LAST = 6
 };
 
 /* gemm_f16_nt with explicit options; opt == NULL means all defaults. */
