@@ -42,6 +42,22 @@ namespace gemm_f16 {
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half4 __attribute__((ext_vector_type(4)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+// Accumulator block and MFMA for each result-block edge.
+template <int MB> struct Mfma;
+template <> struct Mfma<32> {
+    using Acc = floatx16;
+    static __device__ __forceinline__ Acc run(half8 a, half8 b, Acc c) {
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+    }
+};
+template <> struct Mfma<16> {
+    using Acc = floatx4;
+    static __device__ __forceinline__ Acc run(half8 a, half8 b, Acc c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+    }
+};
 typedef int int4v __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
@@ -66,28 +82,34 @@ struct Params {
 // Block-tile configuration: BM x BN output tile, K walked 64 at a time in
 // four 16-wide k steps, WM x WN waves each owning a (BM/WM) x (BN/WN) piece
 // of C made of 32x32 MFMA blocks.
-template <int BM_, int BN_, int WM_, int WN_>
+template <int BM_, int BN_, int WM_, int WN_, int MB_ = 32>
 struct Cfg {
-    static constexpr int BM = BM_, BN = BN_, BK = 64, KS = 4;
+    // MB: edge of the MFMA result block.  32: v_mfma_f32_32x32x16_f16 (k 16
+    // per instruction, 16 fp32 results per lane); 16: v_mfma_f32_16x16x32_f16
+    // (k 32 per instruction, 4 results per lane).
+    static constexpr int MB = MB_, MK = MB_ == 32 ? 16 : 32;
+    static constexpr int BM = BM_, BN = BN_, BK = 64, KS = BK / MK;
+    static constexpr int kPlanes = BK / 16;  // 16-wide k planes per stage
     static constexpr int WM = WM_, WN = WN_;
     static constexpr int kWaves = WM * WN;
     static constexpr int kThreads = kWaves * kWave;
     static constexpr int TM = BM / WM, TN = BN / WN;
-    static constexpr int FM = TM / 32, FN = TN / 32;
+    static constexpr int FM = TM / MB, FN = TN / MB;
     static constexpr int kRowsPerPass = kThreads / 8;  // 8 chunks of 16 B per 64-wide row
     static constexpr int kMinWavesPerEU = kWaves <= 4 ? 1 : kWaves / 4;
-    // LDS: per operand and stage, KS planes of ROWS x 32 B (+ padding).
+    // LDS: per operand and stage, kPlanes planes of ROWS x 32 B (+ padding).
     static constexpr int kPlaneA = BM * 32 + GEMM_PLANE_PAD;
     static constexpr int kPlaneB = BN * 32 + GEMM_PLANE_PAD;
-    static constexpr int kStageA = KS * kPlaneA;
-    static constexpr int kStageB = KS * kPlaneB;
+    static constexpr int kStageA = kPlanes * kPlaneA;
+    static constexpr int kStageB = kPlanes * kPlaneB;
     static constexpr int kLdsB = 2 * kStageA;  // B's two stages follow A's
     static constexpr int kLdsBytes = 2 * kStageA + 2 * kStageB;
-    static_assert(TM % 32 == 0 && TN % 32 == 0, "wave tile must be whole 32x32 blocks");
+    static_assert(MB == 32 || MB == 16, "MFMA block edge");
+    static_assert(TM % MB == 0 && TN % MB == 0, "wave tile must be whole MFMA blocks");
     static_assert(kRowsPerPass % 32 == 0, "passes must keep row bits 2-4 per lane");
     static_assert(BM % kRowsPerPass == 0 && BN % kRowsPerPass == 0, "loader passes");
-    static_assert(kStageA + (KS - 1) * kPlaneA + TM * 32 < 65536 &&
-                      kStageB + (KS - 1) * kPlaneB + TN * 32 < 65536,
+    static_assert(kStageA + (kPlanes - 1) * kPlaneA + TM * 32 < 65536 &&
+                      kStageB + (kPlanes - 1) * kPlaneB + TN * 32 < 65536,
                   "LDS immediates must fit the 16-bit offset field");
     static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
 };
@@ -218,31 +240,39 @@ void gemm_f16_nt_kernel(const Params p) {
     const int wa_lane = la.template lds_lane_offset<C::kPlaneA>();
     const int wb_lane = C::kLdsB + lb.template lds_lane_offset<C::kPlaneB>();
 
-    floatx16 acc[FN][FM];
+    using M = Mfma<C::MB>;
+    typename M::Acc acc[FN][FM];
 #pragma unroll
     for (int j = 0; j < FN; ++j)
 #pragma unroll
-        for (int i = 0; i < FM; ++i) acc[j][i] = floatx16{};
+        for (int i = 0; i < FM; ++i) acc[j][i] = typename M::Acc{};
 
-    // Fragment reads: lane l reads row (wave tile row) + l % 32 at k half
-    // l / 32 of each 16-wide k step.
-    const int frow = lane & 31;
-    const int fhalf = lane >> 5;
-    const int ra_lane = (wm * TM + frow) * 32 + ((fhalf ^ half_swap(frow)) * 16);
-    const int rb_lane = C::kLdsB + (wn * TN + frow) * 32 + ((fhalf ^ half_swap(frow)) * 16);
+    // Fragment reads.  32x32x16: lane l reads row (wave tile row) + l % 32
+    // at k half l / 32 of the step's 16-wide plane.  16x16x32: lane l reads
+    // row + l % 16, k eighth l / 16 of the step's 32-wide k range, i.e.
+    // plane 2 ks + l / 32, half (l / 16) % 2.  Either way the per-lane part
+    // is one register and fragment / step offsets are immediates.
+    constexpr int MB = C::MB;
+    const int frow = lane % MB;
+    const int fhalf = MB == 32 ? (lane >> 5) : ((lane >> 4) & 1);
+    const int fplane = MB == 32 ? 0 : (lane >> 5);
+    const int ra_lane = fplane * C::kPlaneA + (wm * TM + frow) * 32 + ((fhalf ^ half_swap(frow)) * 16);
+    const int rb_lane = C::kLdsB + fplane * C::kPlaneB + (wn * TN + frow) * 32 + ((fhalf ^ half_swap(frow)) * 16);
+    constexpr int kPlanesPerStep = C::MK / 16;
     half8 af[2][FM];
     half8 bf[2][FN];
     auto read_frags = [&](int buf, int stage, int ks) {
         // in the order the MFMAs consume them: B0, A0..A(FM-1), B1..
-        bf[buf][0] = *reinterpret_cast<const half8 *>(smem + rb_lane + stage * C::kStageB + ks * C::kPlaneB);
+        bf[buf][0] = *reinterpret_cast<const half8 *>(smem + rb_lane + stage * C::kStageB +
+                                                      ks * kPlanesPerStep * C::kPlaneB);
 #pragma unroll
         for (int i = 0; i < FM; ++i)
             af[buf][i] = *reinterpret_cast<const half8 *>(smem + ra_lane + stage * C::kStageA +
-                                                          ks * C::kPlaneA + i * 1024);
+                                                          ks * kPlanesPerStep * C::kPlaneA + i * MB * 32);
 #pragma unroll
         for (int j = 1; j < FN; ++j)
             bf[buf][j] = *reinterpret_cast<const half8 *>(smem + rb_lane + stage * C::kStageB +
-                                                          ks * C::kPlaneB + j * 1024);
+                                                          ks * kPlanesPerStep * C::kPlaneB + j * MB * 32);
     };
     auto store_a = [&](int i, int stage) {
         *reinterpret_cast<int4v *>(smem + wa_lane + stage * C::kStageA + i * RPP * 32) = la.regs[i];
@@ -279,7 +309,7 @@ void gemm_f16_nt_kernel(const Params p) {
     lds_barrier();
     read_frags(0, 0, 0);
 
-    // One K-tile of work, as KS 16-wide k steps on stage STAGE, which also
+    // One K-tile of work, as KS k steps (MK wide) on stage STAGE, which also
     // moves the staged K-tile kt+1 into the other stage and refills the
     // staging registers with K-tile kt+2.  Past the last K-tile those moves
     // carry zeros that are never read, so every iteration is the same
@@ -328,9 +358,7 @@ void gemm_f16_nt_kernel(const Params p) {
 #pragma unroll
             for (int j = 0; j < FN; ++j)
 #pragma unroll
-                for (int i = 0; i < FM; ++i)
-                    acc[j][i] = __builtin_amdgcn_mfma_f32_32x32x16_f16(bf[cur][j], af[cur][i], acc[j][i],
-                                                                      0, 0, 0);
+                for (int i = 0; i < FM; ++i) acc[j][i] = M::run(bf[cur][j], af[cur][i], acc[j][i]);
             // Pin the issue order: after each MFMA, an even share of this
             // step's other memory instructions (fragment reads first, then
             // LDS write / global load pairs).
@@ -369,20 +397,22 @@ void gemm_f16_nt_kernel(const Params p) {
         k_iter(S1{}, kt + 1);
     }
 
-    // Epilogue.  32x32 MFMA result layout: lane l, register r holds row
-    // 8*(r/4) + 4*(l/32) + r%4, column l%32 of the block; with the swapped
-    // operands the row is n and the column is m.
-    const int quad = (lane >> 5) * 4;
+    // Epilogue.  MFMA result layout: for 32x32 blocks, lane l register r
+    // holds row 8*(r/4) + 4*(l/32) + r%4, column l%32; for 16x16 blocks,
+    // row 4*(l/16) + r, column l%16.  With the swapped operands the row is n
+    // and the column is m, so each group of 4 registers is 4 consecutive n.
+    constexpr int kGroups = MB == 32 ? 4 : 1;
+    const int quad = MB == 32 ? (lane >> 5) * 4 : (lane >> 4) * 4;
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
-        const int m = m0 + wm * TM + i * 32 + frow;
+        const int m = m0 + wm * TM + i * MB + frow;
         if (m >= p.m) continue;
         _Float16 *crow = p.c + (int64_t)m * p.n;
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
 #pragma unroll
-            for (int g = 0; g < 4; ++g) {
-                const int n = n0 + wn * TN + j * 32 + 8 * g + quad;
+            for (int g = 0; g < kGroups; ++g) {
+                const int n = n0 + wn * TN + j * MB + 8 * g + quad;
                 half4 h;
                 h[0] = (_Float16)acc[j][i][4 * g + 0];
                 h[1] = (_Float16)acc[j][i][4 * g + 1];

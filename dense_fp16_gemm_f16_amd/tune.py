@@ -26,8 +26,14 @@ def main(argv=None) -> int:
     ap.add_argument("--rounds", type=int, default=3)
     ap.add_argument("--reps", type=int, default=10)
     ap.add_argument("--swizzles", default="1,4,8")
+    ap.add_argument("--data", action="store_true",
+                    help="instead: time the automatic configuration on one shape (default 8192^3) "
+                         "with different operand values (zeros, ones, {-8..8}/8, U[0,1], U[-1,1], N(0,1))")
     a = ap.parse_args(argv)
     import torch
+
+    if a.data:
+        return data_sweep(a, torch)
 
     shapes = ([tuple(int(x) for x in s.split(",")) for s in a.shapes] if a.shapes else
               [(w.m, w.n, w.k) for w in inputs.WORKLOADS.values()])
@@ -69,6 +75,45 @@ def main(argv=None) -> int:
         print(json.dumps({"shape": [m, n, k], "best": best[0], "best_us": round(best[1], 2),
                           "auto_tile": auto}), flush=True)
         del A, B, C
+    return 0
+
+
+def data_sweep(a, torch) -> int:
+    """The MFMA clock depends on the operand bits: same kernel, different values."""
+    m, n, k = (tuple(int(x) for x in a.shapes[0].split(",")) if a.shapes else (8192, 8192, 8192))
+    gen = torch.Generator(device="cuda").manual_seed(1)
+    makers = {
+        "zeros": lambda s: torch.zeros(s, device="cuda", dtype=torch.float16),
+        "ones": lambda s: torch.ones(s, device="cuda", dtype=torch.float16),
+        "eighths": lambda s: (torch.randint(-8, 9, s, device="cuda", generator=gen) / 8).half(),
+        "uniform[0,1]": lambda s: torch.rand(s, device="cuda", generator=gen).half(),
+        "uniform[-1,1]": lambda s: (torch.rand(s, device="cuda", generator=gen) * 2 - 1).half(),
+        "normal": lambda s: torch.randn(s, device="cuda", generator=gen).half(),
+    }
+    C = torch.empty((m, n), device="cuda", dtype=torch.float16)
+    stream = torch.cuda.current_stream()
+    data = {name: (f((m, k)), f((n, k))) for name, f in makers.items()}
+    times = {name: [] for name in data}
+    for _ in range(a.rounds):
+        for name, (A, B) in data.items():
+            def run():
+                rc = g.gemm_f16_nt_raw(m, n, k, A.data_ptr(), B.data_ptr(), C.data_ptr(), stream.cuda_stream)
+                if rc != g.OK:
+                    raise g.GemmError(rc)
+            for _ in range(2):
+                run()
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(a.reps)]
+            for e0, e1 in ev:
+                e0.record(stream)
+                run()
+                e1.record(stream)
+            torch.cuda.synchronize()
+            times[name].append(statistics.median(e0.elapsed_time(e1) for e0, e1 in ev))
+    for name, t in times.items():
+        us = statistics.median(t) * 1e3
+        print(json.dumps({"shape": [m, n, k], "operands": name, "us": round(us, 1),
+                          "tflops": round(2.0 * m * n * k / (us * 1e-6) / 1e12, 1)}), flush=True)
     return 0
 
 
