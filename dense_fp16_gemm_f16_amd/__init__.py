@@ -30,8 +30,10 @@ TILE_64x64 = 3
 TILE_256x256_W8 = 4
 TILE_256x128 = 5
 TILE_128x256 = 6
+TILE_128x128_M16 = 7
 TILES = {TILE_256x256: (256, 256), TILE_128x128: (128, 128), TILE_64x64: (64, 64),
-         TILE_256x256_W8: (256, 256), TILE_256x128: (256, 128), TILE_128x256: (128, 256)}
+         TILE_256x256_W8: (256, 256), TILE_256x128: (256, 128), TILE_128x256: (128, 256),
+         TILE_128x128_M16: (128, 128)}
 
 # Every symbol include/gemm_f16.h declares.
 EXPORTS = (

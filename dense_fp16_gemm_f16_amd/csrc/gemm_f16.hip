@@ -444,6 +444,7 @@ using Cfg256w8 = Cfg<256, 256, 4, 2>; // 8 waves, 64x128 each
 using Cfg256x128 = Cfg<256, 128, 2, 2>;
 using Cfg128x256 = Cfg<128, 256, 2, 2>;
 using Cfg128 = Cfg<128, 128, 2, 2>;
+using Cfg128m16 = Cfg<128, 128, 2, 2, 16>;  // v_mfma_f32_16x16x32_f16
 using Cfg64 = Cfg<64, 64, 2, 2>;
 
 struct TileShape {
@@ -457,6 +458,7 @@ static TileShape tile_shape(int tile) {
         case GEMM_F16_TILE_256x128: return {256, 128};
         case GEMM_F16_TILE_128x256: return {128, 256};
         case GEMM_F16_TILE_128x128: return {128, 128};
+        case GEMM_F16_TILE_128x128_M16: return {128, 128};
         default: return {64, 64};
     }
 }
@@ -607,6 +609,7 @@ int gemm_f16_nt_ex(int64_t m, int64_t n, int64_t k, const void *a, const void *b
         case GEMM_F16_TILE_256x128: launch<Cfg256x128>(p, vec, s); break;
         case GEMM_F16_TILE_128x256: launch<Cfg128x256>(p, vec, s); break;
         case GEMM_F16_TILE_128x128: launch<Cfg128>(p, vec, s); break;
+        case GEMM_F16_TILE_128x128_M16: launch<Cfg128m16>(p, vec, s); break;
         default: launch<Cfg64>(p, vec, s); break;
     }
     return hipGetLastError() == hipSuccess ? GEMM_F16_OK : GEMM_F16_EHIP;

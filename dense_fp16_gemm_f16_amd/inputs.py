@@ -18,6 +18,11 @@ Workloads (shapes and value distributions):
 
 The float distributions use numpy's PCG64 generator in float32 and round to
 fp16 with numpy's round-to-nearest-even conversion.
+
+Workloads of the second contract, D = A * B with B [K,N] row-major and an
+fp32 D (the day-78 listing's own), carry ``b_layout == "kn"``: their B is
+drawn as a [K,N] row-major array (for the LCG: A's M*K values, then B's K*N
+values in [K,N] order, exactly as that listing fills its inputs).
 """
 from __future__ import annotations
 
@@ -38,6 +43,7 @@ class Workload:
     k: int
     dist: str  # "eighths" | "normal" | "uniform" | "normal05"
     seed: int
+    b_layout: str = "nk"  # "nk": B is [N,K] (C = A B^T); "kn": B is [K,N] (D = A B)
 
     @property
     def flops(self) -> int:
@@ -52,6 +58,9 @@ WORKLOADS = {
         Workload("gemm_8192_uniform", 8192, 8192, 8192, "uniform", 8192),
         Workload("gemm_16384x4096x2048_normal05", 16384, 4096, 2048, "normal05", 2048),
         Workload("gemm_5000x3000x1000_eighths", 5000, 3000, 1000, "eighths", LCG_SEED),
+        Workload("gemm_nn_256_eighths", 256, 256, 256, "eighths", LCG_SEED, "kn"),
+        Workload("gemm_nn_5000x3000x1000_eighths", 5000, 3000, 1000, "eighths", LCG_SEED, "kn"),
+        Workload("gemm_nn_8192_uniform", 8192, 8192, 8192, "uniform", 8192, "kn"),
     )
 }
 
@@ -80,21 +89,23 @@ def lcg_eighths(count: int, seed: int = LCG_SEED) -> np.ndarray:
     return ((top % 17 - 8).astype(np.float32) / np.float32(8.0)).astype(np.float16)
 
 
-def make_inputs(m: int, n: int, k: int, dist: str, seed: int) -> tuple[np.ndarray, np.ndarray]:
-    """A [m,k] and B [n,k] as C-contiguous float16 arrays."""
+def make_inputs(m: int, n: int, k: int, dist: str, seed: int,
+                b_layout: str = "nk") -> tuple[np.ndarray, np.ndarray]:
+    """A [m,k] and B ([n,k], or [k,n] for b_layout "kn") as C-contiguous float16 arrays."""
+    b_shape = (n, k) if b_layout == "nk" else (k, n)
     if dist == "eighths":
         v = lcg_eighths(m * k + n * k, seed)
-        return v[: m * k].reshape(m, k).copy(), v[m * k:].reshape(n, k).copy()
+        return v[: m * k].reshape(m, k).copy(), v[m * k:].reshape(b_shape).copy()
     rng = np.random.default_rng(seed)
     if dist == "normal":
         a = rng.standard_normal((m, k), dtype=np.float32)
-        b = rng.standard_normal((n, k), dtype=np.float32)
+        b = rng.standard_normal(b_shape, dtype=np.float32)
     elif dist == "normal05":
         a = rng.standard_normal((m, k), dtype=np.float32) * np.float32(0.5)
-        b = rng.standard_normal((n, k), dtype=np.float32) * np.float32(0.5)
+        b = rng.standard_normal(b_shape, dtype=np.float32) * np.float32(0.5)
     elif dist == "uniform":
         a = rng.random((m, k), dtype=np.float32) * np.float32(2.0) - np.float32(1.0)
-        b = rng.random((n, k), dtype=np.float32) * np.float32(2.0) - np.float32(1.0)
+        b = rng.random(b_shape, dtype=np.float32) * np.float32(2.0) - np.float32(1.0)
     else:
         raise ValueError(f"unknown distribution {dist!r}")
     return a.astype(np.float16), b.astype(np.float16)
@@ -102,4 +113,4 @@ def make_inputs(m: int, n: int, k: int, dist: str, seed: int) -> tuple[np.ndarra
 
 def workload_inputs(name: str) -> tuple[np.ndarray, np.ndarray]:
     w = WORKLOADS[name]
-    return make_inputs(w.m, w.n, w.k, w.dist, w.seed)
+    return make_inputs(w.m, w.n, w.k, w.dist, w.seed, w.b_layout)

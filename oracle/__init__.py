@@ -50,6 +50,8 @@ class Oracle:
         lib.oracle_gemm_f16_nt_rows.restype = ctypes.c_int
         lib.oracle_gemm_f16_nt_f64.argtypes = [i64, i64, i64, p, p, p, ctypes.c_int]
         lib.oracle_gemm_f16_nt_f64.restype = ctypes.c_int
+        lib.oracle_gemm_f16_nn_f64.argtypes = [i64, i64, i64, p, p, p, i64, p, p, ctypes.c_int]
+        lib.oracle_gemm_f16_nn_f64.restype = ctypes.c_int
         self.lib = lib
         self.path = path
 
@@ -96,6 +98,28 @@ class Oracle:
         _check(self.lib.oracle_gemm_f16_nt_f64(m, n, k, a.ctypes.data, b.ctypes.data,
                                                c.ctypes.data, nthreads or default_threads()))
         return c
+
+
+    def gemm_f16_nn_f64(self, a, b, rows=None, nthreads=None):
+        """D = A @ B (A [M,K], B [K,N]) in fp64, unrounded, and sum |A[m,k] B[k,n]|.
+
+        Returns (d, dabs), float64 [len(rows) or M, N]."""
+        a, b = _bits(a), _bits(b)
+        m, k = a.shape
+        kb, n = b.shape
+        if kb != k:
+            raise ValueError("K mismatch")
+        if rows is None:
+            r_ptr, nrows = None, m
+        else:
+            r = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+            r_ptr, nrows = r.ctypes.data, r.size
+        d = np.zeros((nrows, n), dtype=np.float64)
+        dabs = np.zeros((nrows, n), dtype=np.float64)
+        _check(self.lib.oracle_gemm_f16_nn_f64(m, n, k, a.ctypes.data, b.ctypes.data, r_ptr, nrows,
+                                               d.ctypes.data, dabs.ctypes.data,
+                                               nthreads or default_threads()))
+        return d, dabs
 
 
 def _load() -> Oracle:
@@ -148,3 +172,9 @@ def gemm_f16_nt_rows(a: np.ndarray, b: np.ndarray, rows, nthreads: int | None = 
 def gemm_f16_nt_f64(a: np.ndarray, b: np.ndarray, nthreads: int | None = None) -> np.ndarray:
     """The unrounded fp64 sums of A @ B^T; returns float64 [M,N]."""
     return _load().gemm_f16_nt_f64(a, b, nthreads)
+
+
+def gemm_f16_nn_f64(a: np.ndarray, b: np.ndarray, rows=None, nthreads: int | None = None):
+    """The day-78 listing's reference: D = A @ B with B [K,N], fp64, unrounded,
+    plus sum |A B|; returns (d, dabs)."""
+    return _load().gemm_f16_nn_f64(a, b, rows, nthreads)

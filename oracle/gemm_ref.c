@@ -25,6 +25,10 @@
  *     applied once, directly from fp64 (never via fp32, which would round
  *     twice).  |x| >= 65520 becomes +-inf; NaN stays NaN.
  *
+ * A second function, oracle_gemm_f16_nn_f64 (end of this file), is the
+ * day-78 listing's reference as printed: D = A * B with B [K,N], fp64 sums
+ * left unrounded.
+ *
  * Parity pins (tests/test_oracle_*.py): exact rational brute force on tiny
  * shapes, the identity / all-ones / one-hot / rank-1 closed forms, an exact
  * integer GEMM on {-8..8}/8 inputs, and the binary16 converter against exact
@@ -195,4 +199,82 @@ int oracle_gemm_f16_nt_f64(int64_t m, int64_t n, int64_t k, const uint16_t *a,
                            const uint16_t *b, double *c64, int nthreads)
 {
     return run(m, n, k, a, b, NULL, c64, NULL, m, nthreads);
+}
+
+/* ---- the day-78 listing's own contract ---------------------------------
+ * "wgmma_gemm.cu" computes D = A * B with A [M,K] row-major, B [K,N]
+ * row-major (its producer reads b[(k)*N + n]) and keeps D in fp32; its CPU
+ * reference (gemmCpu) is a triple loop over m, n, k in double that stores
+ * the double sum unrounded.  This is that loop.  It also returns, per
+ * output, the sum of |A[m][k] * B[k][n]| (in fp64), which bounds the error
+ * of any fp32 summation order: |fl32(sum) - sum| <= gamma_K * sum|p|.     */
+
+typedef struct {
+    int64_t m, n, k;
+    const uint16_t *a, *b;
+    double *d64, *dabs;
+    const int64_t *rows;
+    int64_t row_begin, row_end;
+    const double *table;
+} job_nn_t;
+
+static void *run_rows_nn(void *p)
+{
+    const job_nn_t *j = (const job_nn_t *)p;
+    for (int64_t r = j->row_begin; r < j->row_end; ++r) {
+        const int64_t mi = j->rows ? j->rows[r] : r;
+        for (int64_t ni = 0; ni < j->n; ++ni) {
+            double sum = 0.0, sabs = 0.0;
+            for (int64_t ki = 0; ki < j->k; ++ki) {
+                const double prod = j->table[j->a[mi * j->k + ki]] * j->table[j->b[ki * j->n + ni]];
+                sum += prod;
+                sabs += fabs(prod);
+            }
+            j->d64[r * j->n + ni] = sum;
+            if (j->dabs) j->dabs[r * j->n + ni] = sabs;
+        }
+    }
+    return NULL;
+}
+
+/* Rows `rows` (or all rows when rows == NULL, nrows == m) of D = A * B:
+ * d64 and dabs are [nrows, n].  Returns 0, -1, -2 or -3 as above. */
+int oracle_gemm_f16_nn_f64(int64_t m, int64_t n, int64_t k, const uint16_t *a,
+                           const uint16_t *b, const int64_t *rows, int64_t nrows,
+                           double *d64, double *dabs, int nthreads)
+{
+    if (m < 0 || n < 0 || k < 0 || nrows < 0) return -1;
+    if (!rows && nrows != m) return -1;
+    if (nrows == 0 || n == 0) return 0;
+    if ((k > 0 && (!a || !b)) || !d64) return -2;
+    if (rows) {
+        for (int64_t r = 0; r < nrows; ++r)
+            if (rows[r] < 0 || rows[r] >= m) return -1;
+    }
+    double *table = (double *)malloc(sizeof(double) * 65536);
+    if (!table) return -3;
+    for (int h = 0; h < 65536; ++h) table[h] = oracle_f16_to_f64((uint16_t)h);
+    if (nthreads < 1) nthreads = 1;
+    if (nthreads > nrows) nthreads = (int)nrows;
+    pthread_t *tid = (pthread_t *)malloc(sizeof(pthread_t) * nthreads);
+    job_nn_t *jobs = (job_nn_t *)malloc(sizeof(job_nn_t) * nthreads);
+    if (!tid || !jobs) {
+        free(table); free(tid); free(jobs);
+        return -3;
+    }
+    int started = 0;
+    for (int t = 0; t < nthreads; ++t) {
+        jobs[t] = (job_nn_t){m, n, k, a, b, d64, dabs, rows,
+                             nrows * t / nthreads, nrows * (t + 1) / nthreads, table};
+        if (t == nthreads - 1) {
+            run_rows_nn(&jobs[t]);
+        } else if (pthread_create(&tid[t], NULL, run_rows_nn, &jobs[t]) == 0) {
+            ++started;
+        } else {
+            run_rows_nn(&jobs[t]);
+        }
+    }
+    for (int t = 0; t < started; ++t) pthread_join(tid[t], NULL);
+    free(table); free(tid); free(jobs);
+    return 0;
 }

@@ -64,7 +64,7 @@ def test_argument_checks_return_before_any_hip_call(args, expect):
     assert g.lib().gemm_f16_nt(*args, None) == expect
 
 
-@pytest.mark.parametrize("opt", [(7, 0, -1), (-1, 0, -1), (0, -1, -1), (0, 0, 2), (0, 0, -2)])
+@pytest.mark.parametrize("opt", [(8, 0, -1), (-1, 0, -1), (0, -1, -1), (0, 0, 2), (0, 0, -2)])
 def test_bad_options_rejected(opt):
     assert g.gemm_f16_nt_raw(8, 8, 8, FAKE_A, FAKE_B, FAKE_C, 0, *opt) == g.EINVAL
 

@@ -19,7 +19,8 @@ from tests.test_oracle_gemm import _rand_f16
 SRC = os.path.join(os.path.dirname(oracle.__file__), "gemm_ref.c")
 
 MUTANTS = {
-    "drop_last_k_term": ("ki < j->k; ++ki", "ki + 1 < j->k; ++ki"),
+    "drop_last_k_term": ("ki < j->k; ++ki) {\n                sum += j->table[arow[ki]]",
+                         "ki + 1 < j->k; ++ki) {\n                sum += j->table[arow[ki]]"),
     "subtract_products": ("sum += j->table", "sum -= j->table"),
     "b_read_as_k_by_n": ("j->table[brow[ki]]", "j->table[j->b[(ki * j->n + ni) % (j->n * j->k)]]"),
     "wrong_a_row": ("arow = j->a + mi * j->k", "arow = j->a + ((mi + 1) % j->m) * j->k"),
@@ -28,6 +29,10 @@ MUTANTS = {
     "subnormal_scale": ("ldexp(ax, 24)", "ldexp(ax, 23)"),
     "decode_bias": ("ldexp((double)(1024 + f), e - 25)", "ldexp((double)(1024 + f), e - 24)"),
     "subnormal_threshold": ("if (e < -14)", "if (e < -15)"),
+    "nn_b_read_as_n_by_k": ("j->table[j->b[ki * j->n + ni]]", "j->table[j->b[(ni * j->k + ki) % (j->n * j->k)]]"),
+    "nn_abs_dropped": ("sabs += fabs(prod);", "sabs += prod;"),
+    "nn_sum_skips_first": ("for (int64_t ki = 0; ki < j->k; ++ki) {\n                const double prod",
+                           "for (int64_t ki = 1; ki < j->k; ++ki) {\n                const double prod"),
 }
 
 
@@ -69,6 +74,12 @@ def _pin_failures(orc):
     ae, be = inputs.workload_inputs("gemm_256_eighths")
     if not np.array_equal(orc.gemm_f16_nt(ae, be).view(np.uint16), pins.eighths_exact_bits(ae, be)):
         fails.append("eighths_exact")
+    # the day-78 contract: B [K,N], unrounded sums and sum |A B|
+    an, bn = inputs.workload_inputs("gemm_nn_256_eighths")
+    d, dabs = orc.gemm_f16_nn_f64(an, bn)
+    a8, b8 = an.astype(np.float64) * 8, bn.astype(np.float64) * 8
+    if not np.array_equal(d, (a8 @ b8) / 64.0) or not np.array_equal(dabs, (np.abs(a8) @ np.abs(b8)) / 64.0):
+        fails.append("nn_exact")
     # the converter itself, against numpy's float64 -> float16 on a sweep
     xs = np.concatenate([np.exp2(np.linspace(-26, 16.5, 4001)), [65519.0, 65520.0, 2.0**-15 * 1.3]])
     got = np.array([orc.f64_to_f16(float(x)) for x in xs], dtype=np.uint16)
