@@ -1,4 +1,5 @@
-"""MI355X (gfx950) fp16 GEMM: C = fp16(A @ B^T) with fp32 accumulation.
+"""MI355X (gfx950) fp16 GEMM: C = fp16(A @ B^T) with fp32 accumulation, and the
+second contract D = A @ B (B [K,N], fp32 out).
 
 Thin ctypes binding over ``libgemm_f16.so`` (C ABI declared in
 ``include/gemm_f16.h``).  This module only marshals arguments: shapes,
@@ -39,6 +40,8 @@ TILES = {TILE_256x256: (256, 256), TILE_128x128: (128, 128), TILE_64x64: (64, 64
 EXPORTS = (
     "gemm_f16_nt",
     "gemm_f16_nt_ex",
+    "gemm_f16_nn_f32",
+    "gemm_f16_nn_f32_ex",
     "gemm_f16_status_string",
     "gemm_f16_tile_coord",
     "gemm_f16_select_tile",
@@ -74,6 +77,10 @@ def lib() -> ctypes.CDLL:
     L.gemm_f16_nt.restype = ctypes.c_int
     L.gemm_f16_nt_ex.argtypes = [i64, i64, i64, p, p, p, p, ctypes.POINTER(Options)]
     L.gemm_f16_nt_ex.restype = ctypes.c_int
+    L.gemm_f16_nn_f32.argtypes = [i64, i64, i64, p, p, p, p]
+    L.gemm_f16_nn_f32.restype = ctypes.c_int
+    L.gemm_f16_nn_f32_ex.argtypes = [i64, i64, i64, p, p, p, p, ctypes.POINTER(Options)]
+    L.gemm_f16_nn_f32_ex.restype = ctypes.c_int
     L.gemm_f16_status_string.argtypes = [ctypes.c_int]
     L.gemm_f16_status_string.restype = ctypes.c_char_p
     L.gemm_f16_tile_coord.argtypes = [i64, i64, i64, i32, i32,
@@ -95,6 +102,14 @@ def gemm_f16_nt_raw(m: int, n: int, k: int, a_ptr: int, b_ptr: int, c_ptr: int,
     opt = Options(tile, swizzle, xcd, 0)
     return lib().gemm_f16_nt_ex(m, n, k, a_ptr or None, b_ptr or None, c_ptr or None,
                                 stream or None, ctypes.byref(opt))
+
+
+def gemm_f16_nn_f32_raw(m: int, n: int, k: int, a_ptr: int, b_ptr: int, d_ptr: int,
+                        stream: int = 0, tile: int = TILE_AUTO, swizzle: int = 0, xcd: int = -1) -> int:
+    """Direct call of gemm_f16_nn_f32_ex (D fp32 = A B, B [K,N]); returns the status."""
+    opt = Options(tile, swizzle, xcd, 0)
+    return lib().gemm_f16_nn_f32_ex(m, n, k, a_ptr or None, b_ptr or None, d_ptr or None,
+                                    stream or None, ctypes.byref(opt))
 
 
 def gemm_f16_nt(a, b, out=None, *, stream=None, tile: int = TILE_AUTO, swizzle: int = 0,
@@ -126,6 +141,36 @@ def gemm_f16_nt(a, b, out=None, *, stream=None, tile: int = TILE_AUTO, swizzle: 
     with torch.cuda.device(a.device):
         rc = gemm_f16_nt_raw(m, n, k, a.data_ptr(), b.data_ptr(), out.data_ptr(),
                              stream.cuda_stream, tile, swizzle, xcd)
+    if rc != OK:
+        raise GemmError(rc)
+    return out
+
+
+def gemm_f16_nn_f32(a, b, out=None, *, stream=None, tile: int = TILE_AUTO, swizzle: int = 0,
+                    xcd: int = -1):
+    """D = A @ B in fp32 for CUDA/HIP float16 tensors A [M,K] and B [K,N]."""
+    import torch
+
+    if a.dtype != torch.float16 or b.dtype != torch.float16:
+        raise TypeError("a and b must be float16")
+    if a.dim() != 2 or b.dim() != 2 or a.shape[1] != b.shape[0]:
+        raise ValueError("expected a [M,K] and b [K,N]")
+    if not (a.is_cuda and b.is_cuda) or a.device != b.device:
+        raise ValueError("a and b must be on the same GPU")
+    if not (a.is_contiguous() and b.is_contiguous()):
+        raise ValueError("a and b must be contiguous (row-major)")
+    m, k = a.shape
+    n = b.shape[1]
+    if out is None:
+        out = torch.empty((m, n), dtype=torch.float32, device=a.device)
+    elif (out.dtype != torch.float32 or tuple(out.shape) != (m, n) or not out.is_contiguous()
+          or out.device != a.device):
+        raise ValueError("out must be a contiguous float32 [M,N] tensor on a's device")
+    if stream is None:
+        stream = torch.cuda.current_stream(a.device)
+    with torch.cuda.device(a.device):
+        rc = gemm_f16_nn_f32_raw(m, n, k, a.data_ptr(), b.data_ptr(), out.data_ptr(),
+                                 stream.cuda_stream, tile, swizzle, xcd)
     if rc != OK:
         raise GemmError(rc)
     return out

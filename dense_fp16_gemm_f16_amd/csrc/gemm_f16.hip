@@ -70,13 +70,13 @@ constexpr uint32_t kOutOfRange = 0x80000000u;  // buffer offset past any num_rec
 struct Params {
     const _Float16 *a;
     const _Float16 *b;
-    _Float16 *c;
+    void *c;               // fp16 C (NT) or fp32 D (NN)
     int32_t m, n, k;
     int32_t num_m, num_n;  // block tiles along M and N
     int32_t k_tiles;       // ceil(k / BK)
     int32_t swizzle;
     int32_t xcd;
-    int32_t vec_c;         // C rows allow 8-byte stores (N % 4 == 0, c 8-byte aligned)
+    int32_t vec_c;         // rows of C allow 4-element vector stores (N % 4 == 0, aligned base)
 };
 
 // Block-tile configuration: BM x BN output tile, K walked 64 at a time in
@@ -97,21 +97,9 @@ struct Cfg {
     static constexpr int FM = TM / MB, FN = TN / MB;
     static constexpr int kRowsPerPass = kThreads / 8;  // 8 chunks of 16 B per 64-wide row
     static constexpr int kMinWavesPerEU = kWaves <= 4 ? 1 : kWaves / 4;
-    // LDS: per operand and stage, kPlanes planes of ROWS x 32 B (+ padding).
-    static constexpr int kPlaneA = BM * 32 + GEMM_PLANE_PAD;
-    static constexpr int kPlaneB = BN * 32 + GEMM_PLANE_PAD;
-    static constexpr int kStageA = kPlanes * kPlaneA;
-    static constexpr int kStageB = kPlanes * kPlaneB;
-    static constexpr int kLdsB = 2 * kStageA;  // B's two stages follow A's
-    static constexpr int kLdsBytes = 2 * kStageA + 2 * kStageB;
     static_assert(MB == 32 || MB == 16, "MFMA block edge");
     static_assert(TM % MB == 0 && TN % MB == 0, "wave tile must be whole MFMA blocks");
     static_assert(kRowsPerPass % 32 == 0, "passes must keep row bits 2-4 per lane");
-    static_assert(BM % kRowsPerPass == 0 && BN % kRowsPerPass == 0, "loader passes");
-    static_assert(kStageA + (kPlanes - 1) * kPlaneA + TM * 32 < 65536 &&
-                      kStageB + (kPlanes - 1) * kPlaneB + TN * 32 < 65536,
-                  "LDS immediates must fit the 16-bit offset field");
-    static_assert(kLdsBytes <= 160 * 1024, "LDS budget");
 };
 
 // Which 16-byte half of a 32-byte plane row holds k-half h of row `row`:
@@ -138,39 +126,89 @@ __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-// One operand's K-tile: ROWS x 64 fp16 = ROWS x 8 chunks of 16 bytes.  Each
-// pass of the workgroup covers RPP rows; thread t owns chunk t % 8 of rows
-// t / 8 + RPP * i, so every 8 consecutive lanes read one 128-byte row
-// segment.
-template <int ROWS, int RPP, bool VEC>
-struct TileLoader {
+// ---- operands ---------------------------------------------------------------
+//
+// Both operand kinds share one interface, used by the K loop below:
+//   init(...)          per-lane offsets, descriptors of the block tile
+//   begin_tile(t)      descriptor (and lane mask) for K-tile t; a K-tile at
+//                      or past K gets an empty range, so it reads zeros
+//   load(i)            global -> staging registers, pass i of kPasses
+//   store(smem, i, s)  staging registers -> LDS stage s, pass i
+//   read(smem, s, ks, f)  MFMA fragment f of 16-wide k step ks from stage s:
+//                      8 fp16 per lane, lane l holding k 8*(l/32)..+7 of
+//                      row or column f*32 + l%32 (32x32x16), or k
+//                      8*(l/16)..+7 of row f*16 + l%16 (16x16x32)
+
+// Operand stored [rows, K] row-major in HBM: A, and B of the NT contract.
+// LDS stage: kPlanes k planes of ROWS x 32 bytes (16 k per row) plus
+// GEMM_PLANE_PAD bytes.  Each pass of the workgroup covers RPP rows of the
+// K-tile (ROWS x 64 fp16 = ROWS x 8 chunks of 16 bytes); thread t owns
+// chunk t % 8 of rows t / 8 + RPP * i, so every 8 consecutive lanes read one
+// 128-byte row segment.
+template <class C, int ROWS, int WROWS, bool VEC>
+struct KMajorOperand {
+    static constexpr int RPP = C::kRowsPerPass;
     static constexpr int kPasses = ROWS / RPP;
+    static constexpr int kPlane = ROWS * 32 + GEMM_PLANE_PAD;
+    static constexpr int kStage = C::kPlanes * kPlane;
+    static constexpr int kLdsBytes = 2 * kStage;
+    static constexpr int kPlanesPerStep = C::MK / 16;
+    static_assert(ROWS % RPP == 0, "loader passes");
+    // WROWS: rows of this operand one wave reads fragments from; the read
+    // immediates reach stage + last plane + last fragment of the wave.
+    static_assert(kStage + (C::kPlanes - 1) * kPlane + (WROWS - C::MB) * 32 < 65536,
+                  "LDS immediates must fit the 16-bit offset field");
+
     int4v regs[kPasses];
     uint32_t voff[kPasses];  // VEC: byte offset of this lane's chunk from the K-tile start
-    int chunk, row0;
+    int chunk, row0, k_elems, k_tiles;
+    const _Float16 *tile;
+    uint32_t bytes;
+    __amdgpu_buffer_rsrc_t rsrc0, rsrc_t;
+    uint32_t mask;
+    int k0;
+    int w_lane, r_lane;
 
-    __device__ __forceinline__ void init(int tid, int k_elems) {
+    // base: first row of the block tile; rows_valid: rows of it inside the
+    // matrix; frag_row: first row this wave reads fragments from; lds: byte
+    // offset of this operand's two stages.
+    __device__ __forceinline__ void init(const _Float16 *base, int rows_valid, int K, int kt_count, int tid,
+                                         int lane, int frag_row, int lds) {
         chunk = tid & 7;
         row0 = tid >> 3;
+        k_elems = K;
+        k_tiles = kt_count;
+        tile = base;
+        bytes = (uint32_t)rows_valid * (uint32_t)K * 2u;
+        rsrc0 = make_rsrc(base, bytes);
 #pragma unroll
-        for (int i = 0; i < kPasses; ++i) voff[i] = (uint32_t)((row0 + RPP * i) * k_elems + chunk * 8) * 2u;
+        for (int i = 0; i < kPasses; ++i) voff[i] = (uint32_t)((row0 + RPP * i) * K + chunk * 8) * 2u;
+        w_lane = lds + (chunk >> 1) * kPlane + row0 * 32 + (((chunk & 1) ^ half_swap(row0)) * 16);
+        // fragment reads: 32x32x16 lane l takes row l % 32, k half l / 32 of
+        // the step's plane; 16x16x32 lane l takes row l % 16, plane 2 ks +
+        // l / 32, half (l / 16) % 2.
+        const int frow = lane % C::MB;
+        const int fhalf = C::MB == 32 ? (lane >> 5) : ((lane >> 4) & 1);
+        const int fplane = C::MB == 32 ? 0 : (lane >> 5);
+        r_lane = lds + fplane * kPlane + (frag_row + frow) * 32 + ((fhalf ^ half_swap(frow)) * 16);
     }
 
-    // VEC: 0, or kOutOfRange when this lane's chunk of the K-tile starting
-    // at k0 lies past K (K % 8 == 0 on this path, so a chunk is wholly
-    // inside or wholly past K).  Computed once per K-tile.
-    __device__ __forceinline__ uint32_t k_mask(int k_elems, int k0) const {
-        return (k0 + chunk * 8 >= k_elems) ? kOutOfRange : 0u;
+    // Chunks past K (K % 8 == 0 on the VEC path, so a chunk is wholly inside
+    // or wholly past K) get kOutOfRange and read as zero.
+    __device__ __forceinline__ void begin_tile(int t) {
+        const uint32_t skip = (uint32_t)t * (C::BK * 2);
+        const bool live = t < k_tiles;
+        rsrc_t = make_rsrc(tile + (live ? t * C::BK : 0), (live && bytes > skip) ? bytes - skip : 0u);
+        k0 = t * C::BK;
+        mask = (k0 + chunk * 8 >= k_elems) ? kOutOfRange : 0u;
     }
 
-    // VEC: rsrc_tile starts at this K-tile's first column and `mask` (from
-    // k_mask) pushes chunks past K out of range, so they read as zero.
-    // Scalar: every element is bounds-checked against K and the tile rows.
-    __device__ __forceinline__ void load(int i, __amdgpu_buffer_rsrc_t rsrc_tile, uint32_t mask,
-                                         __amdgpu_buffer_rsrc_t rsrc0, int k_elems, int k0) {
+    __device__ __forceinline__ void load(int i) {
         if constexpr (VEC) {
-            regs[i] = __builtin_amdgcn_raw_buffer_load_b128(rsrc_tile, voff[i] | mask, 0, 0);
+            regs[i] = __builtin_amdgcn_raw_buffer_load_b128(rsrc_t, voff[i] | mask, 0, 0);
         } else {
+            // every element bounds-checked against K; rows past the tile's
+            // valid rows are past num_records
             const int row = row0 + RPP * i;
             const int kc = k0 + chunk * 8;
             union {
@@ -187,24 +225,130 @@ struct TileLoader {
         }
     }
 
-    // LDS byte offset of this lane's chunk in pass 0 (plane = chunk / 2).
-    template <int PLANE>
-    __device__ __forceinline__ int lds_lane_offset() const {
-        return (chunk >> 1) * PLANE + row0 * 32 + (((chunk & 1) ^ half_swap(row0)) * 16);
+    __device__ __forceinline__ void store(char *smem, int i, int stage) const {
+        *reinterpret_cast<int4v *>(smem + w_lane + stage * kStage + i * RPP * 32) = regs[i];
+    }
+
+    __device__ __forceinline__ half8 read(const char *smem, int stage, int ks, int f) const {
+        return *reinterpret_cast<const half8 *>(smem + r_lane + stage * kStage +
+                                                ks * kPlanesPerStep * kPlane + f * C::MB * 32);
     }
 };
 
+// B of the second contract, stored [K, N] row-major in HBM (the layout of
+// the day-78 listing "wgmma_gemm.cu").  LDS stage: the K-tile as 64 rows of
+// BN fp16 (n contiguous), each row padded by 64 bytes.  A 32x32x16 fragment
+// needs 8 consecutive k of one column per lane; two ds_read_b64_tr_b16 give
+// exactly that: within each 16-lane group, lane j reads 4 consecutive n of
+// k-row j/4 and the hardware hands lane i the 4 k values of column i.  With
+// the 64-byte row padding the 4 k-rows of a group and the two groups of a
+// half-wave fall on disjoint banks.  Each pass covers RPP k-rows; thread t
+// owns 16-byte chunk t % (BN/8) of k-row t / (BN/8) + RPP * i, so
+// consecutive lanes read consecutive n (coalesced).
 template <class C, bool VEC>
+struct NMajorB {
+    static constexpr int BN = C::BN, BK = C::BK;
+    static constexpr int kCpr = BN / 8;  // 16-byte chunks per k-row
+    static constexpr int RPP = C::kThreads / kCpr;
+    static constexpr int kPasses = BK / RPP;
+    static constexpr int kPitch = BN * 2 + 64;
+    static constexpr int kStage = BK * kPitch;
+    static constexpr int kLdsBytes = 2 * kStage;
+    static_assert(C::MB == 32, "the transposed B path feeds 32x32x16 MFMAs");
+    static_assert(C::kThreads % kCpr == 0 && BK % RPP == 0, "loader passes");
+    static_assert(15 * kPitch + 4 * kPitch + BN * 2 < 65536, "LDS immediates");
+
+    int4v regs[kPasses];
+    uint32_t voff[kPasses];  // VEC: byte offset from the K-tile's first row; bit 31 set past N
+    int chunk, row0, n_total, k_elems, k_tiles, n0;
+    const _Float16 *b;
+    __amdgpu_buffer_rsrc_t rsrc_t;
+    int k0;
+    int w_lane, r_lane[2];
+
+    __device__ __forceinline__ void init(const _Float16 *bmat, int n_first, int N, int K, int kt_count, int tid,
+                                         int lane, int frag_col, int lds) {
+        chunk = tid % kCpr;
+        row0 = tid / kCpr;
+        n_total = N;
+        k_elems = K;
+        k_tiles = kt_count;
+        n0 = n_first;
+        b = bmat;
+        const uint32_t col_mask = (n0 + chunk * 8 >= N) ? kOutOfRange : 0u;  // N % 8 == 0 on VEC
+#pragma unroll
+        for (int i = 0; i < kPasses; ++i)
+            voff[i] = ((uint32_t)((row0 + RPP * i) * N + n0 + chunk * 8) * 2u) | col_mask;
+        w_lane = lds + row0 * kPitch + chunk * 16;
+        const int g = lane >> 4, j = lane & 15;
+        const int base = lds + (8 * (lane >> 5) + (j >> 2)) * kPitch + (frag_col + 16 * (g & 1) + 4 * (j & 3)) * 2;
+        r_lane[0] = base;
+        r_lane[1] = base + kStage;
+    }
+
+    // K-tile t: k-rows t*BK .. ; the range ends at the last k-row inside K.
+    __device__ __forceinline__ void begin_tile(int t) {
+        k0 = t * BK;
+        const int rows = t < k_tiles ? min(BK, k_elems - k0) : 0;
+        rsrc_t = make_rsrc(b + (t < k_tiles ? (int64_t)k0 * n_total : 0), (uint32_t)rows * (uint32_t)n_total * 2u);
+    }
+
+    __device__ __forceinline__ void load(int i) {
+        if constexpr (VEC) {
+            regs[i] = __builtin_amdgcn_raw_buffer_load_b128(rsrc_t, voff[i], 0, 0);
+        } else {
+            const int row = row0 + RPP * i;
+            const int nc = n0 + chunk * 8;
+            union {
+                short s[8];
+                int4v v;
+            } u;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const uint32_t off = (nc + e < n_total) ? (uint32_t)(row * n_total + nc + e) * 2u : kOutOfRange;
+                u.s[e] = __builtin_amdgcn_raw_buffer_load_b16(rsrc_t, off, 0, 0);
+            }
+            regs[i] = u.v;
+        }
+    }
+
+    __device__ __forceinline__ void store(char *smem, int i, int stage) const {
+        *reinterpret_cast<int4v *>(smem + w_lane + stage * kStage + i * RPP * kPitch) = regs[i];
+    }
+
+    __device__ __forceinline__ half8 read(const char *smem, int stage, int ks, int f) const {
+        typedef __fp16 fp16x4 __attribute__((__vector_size__(4 * sizeof(__fp16))));
+        typedef __attribute__((address_space(3))) fp16x4 lds_fp16x4;
+        char *p0 = const_cast<char *>(smem) + r_lane[stage] + ks * 16 * kPitch + f * 64;
+        // address-space casts of pointers into the __shared__ array
+        const fp16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_fp16x4 *)p0);
+        const fp16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_fp16x4 *)(p0 + 4 * kPitch));
+        half8 r;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            r[e] = (_Float16)lo[e];
+            r[4 + e] = (_Float16)hi[e];
+        }
+        return r;
+    }
+};
+
+// ---- the kernel -----------------------------------------------------------
+//
+// NN == false: C fp16 [M,N] = A [M,K] * B[N,K]^T (the tutorial's contract).
+// NN == true:  D fp32 [M,N] = A [M,K] * B[K,N]   (the day-78 listing's).
+template <class C, bool VEC, bool NN>
 __global__ __launch_bounds__(C::kThreads)
 __attribute__((amdgpu_waves_per_eu(C::kMinWavesPerEU, C::kMinWavesPerEU)))
-void gemm_f16_nt_kernel(const Params p) {
-    constexpr int BM = C::BM, BN = C::BN, BK = C::BK, KS = C::KS;
-    constexpr int TM = C::TM, TN = C::TN, FM = C::FM, FN = C::FN;
-    constexpr int RPP = C::kRowsPerPass;
-    using LoaderA = TileLoader<BM, RPP, VEC>;
-    using LoaderB = TileLoader<BN, RPP, VEC>;
-    constexpr int PA = LoaderA::kPasses, PB = LoaderB::kPasses;
-    __shared__ __attribute__((aligned(1024))) char smem[C::kLdsBytes];
+void gemm_f16_kernel(const Params p) {
+    constexpr int BM = C::BM, BN = C::BN, KS = C::KS;
+    constexpr int TM = C::TM, TN = C::TN, FM = C::FM, FN = C::FN, MB = C::MB;
+    using OpA = KMajorOperand<C, BM, TM, VEC>;
+    using OpB = std::conditional_t<NN, NMajorB<C, VEC>, KMajorOperand<C, BN, TN, VEC>>;
+    constexpr int PA = OpA::kPasses, PB = OpB::kPasses;
+    constexpr int kLdsB = OpA::kLdsBytes;
+    static_assert(OpA::kLdsBytes + OpB::kLdsBytes <= 160 * 1024, "LDS budget");
+    __shared__ __attribute__((aligned(1024))) char smem[OpA::kLdsBytes + OpB::kLdsBytes];
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
@@ -215,97 +359,54 @@ void gemm_f16_nt_kernel(const Params p) {
     const TileCoord tc = tile_coord(blockIdx.x, p.num_m, p.num_n, p.swizzle, p.xcd != 0);
     const int m0 = (int)tc.m_block * BM;
     const int n0 = (int)tc.n_block * BN;
+    const int kt_count = p.k_tiles;
+    if (kt_count == 0) return;  // never launched with K == 0
 
     // Per-tile buffer descriptors: rows past M (N) lie beyond num_records.
-    const int rows_a = min(BM, p.m - m0);
-    const int rows_b = min(BN, p.n - n0);
-    const _Float16 *a_tile = p.a + (int64_t)m0 * p.k;
-    const _Float16 *b_tile = p.b + (int64_t)n0 * p.k;
-    const uint32_t bytes_a = (uint32_t)rows_a * (uint32_t)p.k * 2u;
-    const uint32_t bytes_b = (uint32_t)rows_b * (uint32_t)p.k * 2u;
-    const __amdgpu_buffer_rsrc_t ra0 = make_rsrc(a_tile, bytes_a);
-    const __amdgpu_buffer_rsrc_t rb0 = make_rsrc(b_tile, bytes_b);
-    // Descriptor of K-tile t: starts t*BK columns in and its range shrinks
-    // to match; a K-tile at or past K (fetched by the last iterations, never
-    // used) gets an empty range, so nothing is read.
-    auto rsrc_at = [&](const _Float16 *tile, uint32_t bytes, int t) {
-        const uint32_t skip = (uint32_t)t * (BK * 2);
-        return make_rsrc(tile + (t < p.k_tiles ? t * BK : 0), (t < p.k_tiles && bytes > skip) ? bytes - skip : 0u);
-    };
+    OpA opa;
+    OpB opb;
+    opa.init(p.a + (int64_t)m0 * p.k, min(BM, p.m - m0), p.k, kt_count, tid, lane, wm * TM, 0);
+    if constexpr (NN)
+        opb.init(p.b, n0, p.n, p.k, kt_count, tid, lane, wn * TN, kLdsB);
+    else
+        opb.init(p.b + (int64_t)n0 * p.k, min(BN, p.n - n0), p.k, kt_count, tid, lane, wn * TN, kLdsB);
 
-    LoaderA la;
-    LoaderB lb;
-    la.init(tid, p.k);
-    lb.init(tid, p.k);
-    const int wa_lane = la.template lds_lane_offset<C::kPlaneA>();
-    const int wb_lane = C::kLdsB + lb.template lds_lane_offset<C::kPlaneB>();
-
-    using M = Mfma<C::MB>;
+    using M = Mfma<MB>;
     typename M::Acc acc[FN][FM];
 #pragma unroll
     for (int j = 0; j < FN; ++j)
 #pragma unroll
         for (int i = 0; i < FM; ++i) acc[j][i] = typename M::Acc{};
 
-    // Fragment reads.  32x32x16: lane l reads row (wave tile row) + l % 32
-    // at k half l / 32 of the step's 16-wide plane.  16x16x32: lane l reads
-    // row + l % 16, k eighth l / 16 of the step's 32-wide k range, i.e.
-    // plane 2 ks + l / 32, half (l / 16) % 2.  Either way the per-lane part
-    // is one register and fragment / step offsets are immediates.
-    constexpr int MB = C::MB;
-    const int frow = lane % MB;
-    const int fhalf = MB == 32 ? (lane >> 5) : ((lane >> 4) & 1);
-    const int fplane = MB == 32 ? 0 : (lane >> 5);
-    const int ra_lane = fplane * C::kPlaneA + (wm * TM + frow) * 32 + ((fhalf ^ half_swap(frow)) * 16);
-    const int rb_lane = C::kLdsB + fplane * C::kPlaneB + (wn * TN + frow) * 32 + ((fhalf ^ half_swap(frow)) * 16);
-    constexpr int kPlanesPerStep = C::MK / 16;
     half8 af[2][FM];
     half8 bf[2][FN];
     auto read_frags = [&](int buf, int stage, int ks) {
         // in the order the MFMAs consume them: B0, A0..A(FM-1), B1..
-        bf[buf][0] = *reinterpret_cast<const half8 *>(smem + rb_lane + stage * C::kStageB +
-                                                      ks * kPlanesPerStep * C::kPlaneB);
+        bf[buf][0] = opb.read(smem, stage, ks, 0);
 #pragma unroll
-        for (int i = 0; i < FM; ++i)
-            af[buf][i] = *reinterpret_cast<const half8 *>(smem + ra_lane + stage * C::kStageA +
-                                                          ks * kPlanesPerStep * C::kPlaneA + i * MB * 32);
+        for (int i = 0; i < FM; ++i) af[buf][i] = opa.read(smem, stage, ks, i);
 #pragma unroll
-        for (int j = 1; j < FN; ++j)
-            bf[buf][j] = *reinterpret_cast<const half8 *>(smem + rb_lane + stage * C::kStageB +
-                                                          ks * kPlanesPerStep * C::kPlaneB + j * MB * 32);
+        for (int j = 1; j < FN; ++j) bf[buf][j] = opb.read(smem, stage, ks, j);
     };
-    auto store_a = [&](int i, int stage) {
-        *reinterpret_cast<int4v *>(smem + wa_lane + stage * C::kStageA + i * RPP * 32) = la.regs[i];
-    };
-    auto store_b = [&](int i, int stage) {
-        *reinterpret_cast<int4v *>(smem + wb_lane + stage * C::kStageB + i * RPP * 32) = lb.regs[i];
-    };
-
-    const int kt_count = p.k_tiles;
-    if (kt_count == 0) return;  // never launched with K == 0
 
     // Prologue: K-tile 0 into stage 0, K-tile 1 (zeros if K has one K-tile)
     // into the staging registers.
-    {
-        const __amdgpu_buffer_rsrc_t a_t = rsrc_at(a_tile, bytes_a, 0), b_t = rsrc_at(b_tile, bytes_b, 0);
-        const uint32_t ma = la.k_mask(p.k, 0), mb = lb.k_mask(p.k, 0);
+    opa.begin_tile(0);
+    opb.begin_tile(0);
 #pragma unroll
-        for (int i = 0; i < PA; ++i) la.load(i, a_t, ma, ra0, p.k, 0);
+    for (int i = 0; i < PA; ++i) opa.load(i);
 #pragma unroll
-        for (int i = 0; i < PB; ++i) lb.load(i, b_t, mb, rb0, p.k, 0);
+    for (int i = 0; i < PB; ++i) opb.load(i);
 #pragma unroll
-        for (int i = 0; i < PA; ++i) store_a(i, 0);
+    for (int i = 0; i < PA; ++i) opa.store(smem, i, 0);
 #pragma unroll
-        for (int i = 0; i < PB; ++i) store_b(i, 0);
-    }
-    {
-        const __amdgpu_buffer_rsrc_t a_t = rsrc_at(a_tile, bytes_a, 1), b_t = rsrc_at(b_tile, bytes_b, 1);
-        const uint32_t ma = la.k_mask(p.k, BK), mb = lb.k_mask(p.k, BK);
+    for (int i = 0; i < PB; ++i) opb.store(smem, i, 0);
+    opa.begin_tile(1);
+    opb.begin_tile(1);
 #pragma unroll
-        for (int i = 0; i < PA; ++i) la.load(i, a_t, ma, ra0, p.k, BK);
+    for (int i = 0; i < PA; ++i) opa.load(i);
 #pragma unroll
-        for (int i = 0; i < PB; ++i) lb.load(i, b_t, mb, rb0, p.k, BK);
-    }
+    for (int i = 0; i < PB; ++i) opb.load(i);
     lds_barrier();
     read_frags(0, 0, 0);
 
@@ -324,10 +425,8 @@ void gemm_f16_nt_kernel(const Params p) {
     auto k_iter = [&](auto stage_tag, int kt) {
         constexpr int STAGE = decltype(stage_tag)::value;
         constexpr int NXT = STAGE ^ 1;
-        const int k_load = (kt + 2) * BK;
-        const __amdgpu_buffer_rsrc_t a_t = rsrc_at(a_tile, bytes_a, kt + 2);
-        const __amdgpu_buffer_rsrc_t b_t = rsrc_at(b_tile, bytes_b, kt + 2);
-        const uint32_t ma = la.k_mask(p.k, k_load), mb = lb.k_mask(p.k, k_load);
+        opa.begin_tile(kt + 2);
+        opb.begin_tile(kt + 2);
 #pragma unroll
         for (int ks = 0; ks < KS; ++ks) {
             const int cur = ks & 1;
@@ -343,18 +442,18 @@ void gemm_f16_nt_kernel(const Params p) {
             if (ks < kSlices) {
 #pragma unroll
                 for (int i = ks * PA / kSlices; i < (ks + 1) * PA / kSlices; ++i) {
-                    store_a(i, NXT);
-                    la.load(i, a_t, ma, ra0, p.k, k_load);
+                    opa.store(smem, i, NXT);
+                    opa.load(i);
                 }
 #pragma unroll
                 for (int i = ks * PB / kSlices; i < (ks + 1) * PB / kSlices; ++i) {
-                    store_b(i, NXT);
-                    lb.load(i, b_t, mb, rb0, p.k, k_load);
+                    opb.store(smem, i, NXT);
+                    opb.load(i);
                 }
             }
-            // B rows feed the MFMA's A operand and A rows its B operand, so
-            // each 32x32 result block is C^T: a lane then holds 4
-            // consecutive n of one m row, which stores as 8 bytes.
+            // B fragments feed the MFMA's A operand and A fragments its B
+            // operand, so each result block is C^T: a lane then holds 4
+            // consecutive n of one m row, which store as one vector.
 #pragma unroll
             for (int j = 0; j < FN; ++j)
 #pragma unroll
@@ -363,7 +462,7 @@ void gemm_f16_nt_kernel(const Params p) {
             // step's other memory instructions (fragment reads first, then
             // LDS write / global load pairs).
             {
-                const int nr = FM + FN;
+                const int nr = NN ? FM + 2 * FN : FM + FN;
                 const int nw = ks < kSlices ? ((ks + 1) * PA / kSlices - ks * PA / kSlices) +
                                                   ((ks + 1) * PB / kSlices - ks * PB / kSlices)
                                             : 0;
@@ -402,39 +501,55 @@ void gemm_f16_nt_kernel(const Params p) {
     // row 4*(l/16) + r, column l%16.  With the swapped operands the row is n
     // and the column is m, so each group of 4 registers is 4 consecutive n.
     constexpr int kGroups = MB == 32 ? 4 : 1;
+    const int frow = lane % MB;
     const int quad = MB == 32 ? (lane >> 5) * 4 : (lane >> 4) * 4;
 #pragma unroll
     for (int i = 0; i < FM; ++i) {
         const int m = m0 + wm * TM + i * MB + frow;
         if (m >= p.m) continue;
-        _Float16 *crow = p.c + (int64_t)m * p.n;
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
 #pragma unroll
             for (int g = 0; g < kGroups; ++g) {
                 const int n = n0 + wn * TN + j * MB + 8 * g + quad;
-                half4 h;
-                h[0] = (_Float16)acc[j][i][4 * g + 0];
-                h[1] = (_Float16)acc[j][i][4 * g + 1];
-                h[2] = (_Float16)acc[j][i][4 * g + 2];
-                h[3] = (_Float16)acc[j][i][4 * g + 3];
-                if (p.vec_c && n + 3 < p.n) {
-                    *reinterpret_cast<half4 *>(crow + n) = h;
-                } else {
+                if constexpr (NN) {
+                    // fp32 out: the accumulator itself, unrounded
+                    float *drow = static_cast<float *>(p.c) + (int64_t)m * p.n;
+                    const floatx4 v = {acc[j][i][4 * g + 0], acc[j][i][4 * g + 1], acc[j][i][4 * g + 2],
+                                       acc[j][i][4 * g + 3]};
+                    if (p.vec_c && n + 3 < p.n) {
+                        *reinterpret_cast<floatx4 *>(drow + n) = v;
+                    } else {
 #pragma unroll
-                    for (int e = 0; e < 4; ++e)
-                        if (n + e < p.n) crow[n + e] = h[e];
+                        for (int e = 0; e < 4; ++e)
+                            if (n + e < p.n) drow[n + e] = v[e];
+                    }
+                } else {
+                    _Float16 *crow = static_cast<_Float16 *>(p.c) + (int64_t)m * p.n;
+                    half4 h;
+                    h[0] = (_Float16)acc[j][i][4 * g + 0];
+                    h[1] = (_Float16)acc[j][i][4 * g + 1];
+                    h[2] = (_Float16)acc[j][i][4 * g + 2];
+                    h[3] = (_Float16)acc[j][i][4 * g + 3];
+                    if (p.vec_c && n + 3 < p.n) {
+                        *reinterpret_cast<half4 *>(crow + n) = h;
+                    } else {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e)
+                            if (n + e < p.n) crow[n + e] = h[e];
+                    }
                 }
             }
         }
     }
 }
 
-// Fill C with +0 (K == 0: the zero accumulator is what gets stored).
-__global__ __launch_bounds__(256) void fill_zero_kernel(_Float16 *c, int64_t count) {
+// Fill the output with +0 (K == 0: the zero accumulator is what gets stored).
+template <class T>
+__global__ __launch_bounds__(256) void fill_zero_kernel(T *c, int64_t count) {
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < count; i += stride)
-        c[i] = (_Float16)0.0f;
+        c[i] = (T)0.0f;
 }
 
 // ---- host side --------------------------------------------------------------
@@ -529,13 +644,89 @@ static int check_device() {
     return cached[dev] == 1 ? GEMM_F16_OK : GEMM_F16_EDEVICE;
 }
 
-template <class C>
+template <class C, bool NN>
 static void launch(const Params &p, bool vec, hipStream_t stream) {
     const dim3 grid((unsigned)((int64_t)p.num_m * p.num_n));
     if (vec)
-        hipLaunchKernelGGL((gemm_f16_nt_kernel<C, true>), grid, dim3(C::kThreads), 0, stream, p);
+        hipLaunchKernelGGL((gemm_f16_kernel<C, true, NN>), grid, dim3(C::kThreads), 0, stream, p);
     else
-        hipLaunchKernelGGL((gemm_f16_nt_kernel<C, false>), grid, dim3(C::kThreads), 0, stream, p);
+        hipLaunchKernelGGL((gemm_f16_kernel<C, false, NN>), grid, dim3(C::kThreads), 0, stream, p);
+}
+
+template <bool NN>
+static void launch_tile(int tile, const Params &p, bool vec, hipStream_t s) {
+    switch (tile) {
+        case GEMM_F16_TILE_256x256: launch<Cfg256, NN>(p, vec, s); break;
+        case GEMM_F16_TILE_256x256_W8: launch<Cfg256w8, NN>(p, vec, s); break;
+        case GEMM_F16_TILE_256x128: launch<Cfg256x128, NN>(p, vec, s); break;
+        case GEMM_F16_TILE_128x256: launch<Cfg128x256, NN>(p, vec, s); break;
+        case GEMM_F16_TILE_128x128: launch<Cfg128, NN>(p, vec, s); break;
+        default: launch<Cfg64, NN>(p, vec, s); break;
+    }
+}
+
+// Both contracts: NN == false is C fp16 = A B^T (B [N,K]); NN == true is
+// D fp32 = A B (B [K,N]).
+static int gemm_impl(bool nn, int64_t m, int64_t n, int64_t k, const void *a, const void *b, void *c,
+                     void *stream, const gemm_f16_options *opt) {
+    int rc = check_sizes(m, n, k);
+    if (rc != GEMM_F16_OK) return rc;
+    if (nn && n >= (int64_t(1) << 25)) return GEMM_F16_EINVAL;
+    gemm_f16_options o = {0, 0, -1, 0};
+    if (opt) o = *opt;
+    if (o.tile < 0 || o.tile > GEMM_F16_TILE_LAST || o.swizzle < 0 || o.xcd < -1 || o.xcd > 1)
+        return GEMM_F16_EINVAL;
+    if (nn && o.tile == GEMM_F16_TILE_128x128_M16) return GEMM_F16_EINVAL;
+    if (m == 0 || n == 0) return GEMM_F16_OK;
+    if (!c || (k > 0 && (!a || !b))) return GEMM_F16_ENULL;
+    const int out_bytes = nn ? 4 : 2;
+    if (((uintptr_t)c & (out_bytes - 1)) || ((uintptr_t)a & 1) || ((uintptr_t)b & 1)) return GEMM_F16_EALIGN;
+    if (k > 0 && (ranges_overlap(c, m * n * out_bytes, a, m * k * 2) ||
+                  ranges_overlap(c, m * n * out_bytes, b, n * k * 2)))
+        return GEMM_F16_EOVERLAP;
+    rc = check_device();
+    if (rc != GEMM_F16_OK) return rc;
+    hipStream_t s = (hipStream_t)stream;
+
+    if (k == 0) {
+        const int64_t count = m * n;
+        const unsigned blocks = (unsigned)std::min<int64_t>(cdiv(count, 256), 4096);
+        if (nn)
+            hipLaunchKernelGGL(fill_zero_kernel<float>, dim3(blocks), dim3(256), 0, s, (float *)c, count);
+        else
+            hipLaunchKernelGGL(fill_zero_kernel<_Float16>, dim3(blocks), dim3(256), 0, s, (_Float16 *)c, count);
+        return hipGetLastError() == hipSuccess ? GEMM_F16_OK : GEMM_F16_EHIP;
+    }
+
+    const int tile = o.tile ? o.tile : auto_tile(m, n);
+    const TileShape ts = tile_shape(tile);
+    Params p;
+    p.a = (const _Float16 *)a;
+    p.b = (const _Float16 *)b;
+    p.c = c;
+    p.m = (int32_t)m;
+    p.n = (int32_t)n;
+    p.k = (int32_t)k;
+    p.num_m = (int32_t)cdiv(m, ts.bm);
+    p.num_n = (int32_t)cdiv(n, ts.bn);
+    p.k_tiles = (int32_t)cdiv(k, 64);
+    p.swizzle = o.swizzle ? o.swizzle : 4;
+    p.xcd = o.xcd < 0 ? 1 : o.xcd;
+    // 4-element vector stores: 8 bytes (fp16) or 16 bytes (fp32)
+    p.vec_c = ((n % 4) == 0 && ((uintptr_t)c % (4 * out_bytes)) == 0) ? 1 : 0;
+    // 16-byte loads need 16-byte aligned rows of A, and of B in its layout
+    const bool vec = (k % 8) == 0 && (!nn || (n % 8) == 0) && ((uintptr_t)a % 16) == 0 &&
+                     ((uintptr_t)b % 16) == 0;
+    if ((int64_t)p.num_m * p.num_n >= (int64_t(1) << 31)) return GEMM_F16_EINVAL;
+
+    if (nn) {
+        launch_tile<true>(tile, p, vec, s);
+    } else if (tile == GEMM_F16_TILE_128x128_M16) {
+        launch<Cfg128m16, false>(p, vec, s);
+    } else {
+        launch_tile<false>(tile, p, vec, s);
+    }
+    return hipGetLastError() == hipSuccess ? GEMM_F16_OK : GEMM_F16_EHIP;
 }
 
 }  // namespace gemm_f16
@@ -563,61 +754,22 @@ int gemm_f16_tile_coord(int64_t pid, int64_t num_m, int64_t num_n, int32_t swizz
 
 int gemm_f16_nt_ex(int64_t m, int64_t n, int64_t k, const void *a, const void *b, void *c,
                    void *stream, const gemm_f16_options *opt) {
-    int rc = check_sizes(m, n, k);
-    if (rc != GEMM_F16_OK) return rc;
-    gemm_f16_options o = {0, 0, -1, 0};
-    if (opt) o = *opt;
-    if (o.tile < 0 || o.tile > GEMM_F16_TILE_LAST || o.swizzle < 0 || o.xcd < -1 || o.xcd > 1)
-        return GEMM_F16_EINVAL;
-    if (m == 0 || n == 0) return GEMM_F16_OK;
-    if (!c || (k > 0 && (!a || !b))) return GEMM_F16_ENULL;
-    if (((uintptr_t)c & 1) || ((uintptr_t)a & 1) || ((uintptr_t)b & 1)) return GEMM_F16_EALIGN;
-    if (k > 0 && (ranges_overlap(c, m * n * 2, a, m * k * 2) || ranges_overlap(c, m * n * 2, b, n * k * 2)))
-        return GEMM_F16_EOVERLAP;
-    rc = check_device();
-    if (rc != GEMM_F16_OK) return rc;
-    hipStream_t s = (hipStream_t)stream;
-
-    if (k == 0) {
-        const int64_t count = m * n;
-        const unsigned blocks = (unsigned)std::min<int64_t>(cdiv(count, 256), 4096);
-        hipLaunchKernelGGL(fill_zero_kernel, dim3(blocks), dim3(256), 0, s, (_Float16 *)c, count);
-        return hipGetLastError() == hipSuccess ? GEMM_F16_OK : GEMM_F16_EHIP;
-    }
-
-    const int tile = o.tile ? o.tile : auto_tile(m, n);
-    const TileShape ts = tile_shape(tile);
-    Params p;
-    p.a = (const _Float16 *)a;
-    p.b = (const _Float16 *)b;
-    p.c = (_Float16 *)c;
-    p.m = (int32_t)m;
-    p.n = (int32_t)n;
-    p.k = (int32_t)k;
-    p.num_m = (int32_t)cdiv(m, ts.bm);
-    p.num_n = (int32_t)cdiv(n, ts.bn);
-    p.k_tiles = (int32_t)cdiv(k, 64);
-    p.swizzle = o.swizzle ? o.swizzle : 4;
-    p.xcd = o.xcd < 0 ? 1 : o.xcd;
-    p.vec_c = ((n % 4) == 0 && ((uintptr_t)c % 8) == 0) ? 1 : 0;
-    const bool vec = (k % 8) == 0 && ((uintptr_t)a % 16) == 0 && ((uintptr_t)b % 16) == 0;
-    if ((int64_t)p.num_m * p.num_n >= (int64_t(1) << 31)) return GEMM_F16_EINVAL;
-
-    switch (tile) {
-        case GEMM_F16_TILE_256x256: launch<Cfg256>(p, vec, s); break;
-        case GEMM_F16_TILE_256x256_W8: launch<Cfg256w8>(p, vec, s); break;
-        case GEMM_F16_TILE_256x128: launch<Cfg256x128>(p, vec, s); break;
-        case GEMM_F16_TILE_128x256: launch<Cfg128x256>(p, vec, s); break;
-        case GEMM_F16_TILE_128x128: launch<Cfg128>(p, vec, s); break;
-        case GEMM_F16_TILE_128x128_M16: launch<Cfg128m16>(p, vec, s); break;
-        default: launch<Cfg64>(p, vec, s); break;
-    }
-    return hipGetLastError() == hipSuccess ? GEMM_F16_OK : GEMM_F16_EHIP;
+    return gemm_impl(false, m, n, k, a, b, c, stream, opt);
 }
 
 int gemm_f16_nt(int64_t m, int64_t n, int64_t k, const void *a, const void *b, void *c,
                 void *stream) {
-    return gemm_f16_nt_ex(m, n, k, a, b, c, stream, nullptr);
+    return gemm_impl(false, m, n, k, a, b, c, stream, nullptr);
+}
+
+int gemm_f16_nn_f32_ex(int64_t m, int64_t n, int64_t k, const void *a, const void *b, void *d,
+                       void *stream, const gemm_f16_options *opt) {
+    return gemm_impl(true, m, n, k, a, b, d, stream, opt);
+}
+
+int gemm_f16_nn_f32(int64_t m, int64_t n, int64_t k, const void *a, const void *b, void *d,
+                    void *stream) {
+    return gemm_impl(true, m, n, k, a, b, d, stream, nullptr);
 }
 
 const char *gemm_f16_status_string(int status) {
@@ -625,10 +777,10 @@ const char *gemm_f16_status_string(int status) {
         case GEMM_F16_OK: return "ok";
         case GEMM_F16_EINVAL: return "invalid argument (size out of range or bad option)";
         case GEMM_F16_ENULL: return "null pointer with a non-empty extent";
-        case GEMM_F16_EALIGN: return "pointer not 2-byte aligned";
+        case GEMM_F16_EALIGN: return "pointer not aligned to its element size";
         case GEMM_F16_EDEVICE: return "current device is not gfx950 (MI355X)";
         case GEMM_F16_EHIP: return "HIP runtime error or kernel launch failure";
-        case GEMM_F16_EOVERLAP: return "c overlaps a or b";
+        case GEMM_F16_EOVERLAP: return "the output overlaps a or b";
         default: return "unknown status";
     }
 }

@@ -42,12 +42,12 @@ extern "C" {
 
 enum {
     GEMM_F16_OK = 0,
-    GEMM_F16_EINVAL = -1,     /* negative size, size product overflow, K >= 2^22, bad option */
+    GEMM_F16_EINVAL = -1,     /* negative size, M or N >= 2^31, K >= 2^22, bad option */
     GEMM_F16_ENULL = -2,      /* null pointer with a non-empty extent */
-    GEMM_F16_EALIGN = -3,     /* pointer not 2-byte aligned */
+    GEMM_F16_EALIGN = -3,     /* pointer not aligned to its element size (2 or 4 bytes) */
     GEMM_F16_EDEVICE = -4,    /* current device is not gfx950 */
     GEMM_F16_EHIP = -5,       /* a HIP runtime call or the kernel launch failed */
-    GEMM_F16_EOVERLAP = -6    /* c overlaps a or b */
+    GEMM_F16_EOVERLAP = -6    /* the output overlaps a or b */
 };
 
 /*
@@ -98,6 +98,26 @@ enum {
 /* gemm_f16_nt with explicit options; opt == NULL means all defaults. */
 int gemm_f16_nt_ex(int64_t m, int64_t n, int64_t k, const void *a, const void *b,
                    void *c, void *stream, const gemm_f16_options *opt);
+
+/*
+ * The second contract, that of the day-78 listing "wgmma_gemm.cu" (its
+ * kernel, its B layout and its fp32 output):
+ *
+ *     D[m][n] = sum_{k<K} A[m][k] * B[k][n]      fp32 accumulation, fp32 out
+ *
+ *   a  fp16 [M,K] row-major      element (m,k) at a[m*K + k]
+ *   b  fp16 [K,N] row-major      element (k,n) at b[k*N + n]
+ *   d  fp32 [M,N] row-major      element (m,n) at d[m*N + n], 4-byte aligned
+ *
+ * D is the fp32 accumulator itself (no rounding to fp16).  Same sizes,
+ * ownership, asynchrony and error rules as gemm_f16_nt, plus n < 2^25;
+ * k == 0 fills D with +0.  Options as for gemm_f16_nt_ex, except that
+ * GEMM_F16_TILE_128x128_M16 is not available (GEMM_F16_EINVAL).
+ */
+int gemm_f16_nn_f32(int64_t m, int64_t n, int64_t k, const void *a, const void *b,
+                    void *d, void *stream);
+int gemm_f16_nn_f32_ex(int64_t m, int64_t n, int64_t k, const void *a, const void *b,
+                       void *d, void *stream, const gemm_f16_options *opt);
 
 /* Static message for a status code (never NULL). */
 const char *gemm_f16_status_string(int status);

@@ -106,3 +106,21 @@ def test_python_wrapper_refuses_cpu_tensors():
         g.gemm_f16_nt(a, a)
     with pytest.raises(TypeError):
         g.gemm_f16_nt(a.float(), a.float())
+
+
+@pytest.mark.parametrize(
+    "args, expect",
+    [
+        ((4, 4, 4, FAKE_A, FAKE_B, FAKE_C + 2), g.EALIGN),          # fp32 output needs 4-byte alignment
+        ((4, 1 << 25, 4, FAKE_A, FAKE_B, FAKE_C), g.EINVAL),
+        ((4, 4, 4, FAKE_A, FAKE_B, FAKE_A + 16), g.EOVERLAP),
+        ((0, 4, 4, FAKE_A, FAKE_B, FAKE_C), g.OK),
+        ((4, 4, 4, 0, FAKE_B, FAKE_C), g.ENULL),
+    ],
+)
+def test_nn_argument_checks(args, expect):
+    assert g.lib().gemm_f16_nn_f32(*args, None) == expect
+
+
+def test_nn_rejects_the_16x16_tile():
+    assert g.gemm_f16_nn_f32_raw(8, 8, 8, FAKE_A, FAKE_B, FAKE_C, 0, g.TILE_128x128_M16) == g.EINVAL

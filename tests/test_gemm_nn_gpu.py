@@ -1,0 +1,175 @@
+"""Parity of the second contract, D fp32 = A * B with B [K,N] (the day-78
+listing "wgmma_gemm.cu"), against its CPU reference, through the C ABI.
+
+Bars (written here, from the arithmetic):
+* {-8..8}/8 inputs, identity, one-hot: bit-exact.  Every partial sum is a
+  multiple of 1/64 below 2^24, so any fp32 summation order gives the exact
+  sum, which fp32 D holds exactly.  The listing's own gate, |gpu - ref| /
+  max(|ref|, 1) <= 1e-3, is checked as well.
+* random inputs: |D - D_ref| <= 2 * gamma_K * sum_k |A[m,k] B[k,n]| with
+  gamma_K = K u / (1 - K u), u = 2^-24: the classical bound on the error of
+  any order of K fp32 additions (doubled to cover an MFMA that rounds its
+  partial sums less carefully than round-to-nearest), with the sum of
+  |products| from the oracle.
+"""
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import dense_fp16_gemm_f16_amd as g  # noqa: E402
+import oracle  # noqa: E402
+from dense_fp16_gemm_f16_amd import inputs  # noqa: E402
+from tests import pins  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+GUARD = 32  # fp32 elements of sentinel on each side of D
+SENTINEL = np.float32(-12345.5)
+NN_TILES = [t for t in sorted(g.TILES) if t != g.TILE_128x128_M16]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    g.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+def _announce(*what):
+    print("case:", *what, flush=True)
+
+
+def run_nn(a_np, b_np, a_offset=0, b_offset=0, **opts):
+    m, k = a_np.shape
+    kb, n = b_np.shape
+    assert kb == k
+    dev = torch.device("cuda")
+    a_buf = torch.zeros(a_offset + m * k + 8, dtype=torch.float16, device=dev)
+    b_buf = torch.zeros(b_offset + k * n + 8, dtype=torch.float16, device=dev)
+    if m * k:
+        a_buf[a_offset:a_offset + m * k] = torch.from_numpy(a_np.reshape(-1)).to(dev)
+    if k * n:
+        b_buf[b_offset:b_offset + k * n] = torch.from_numpy(b_np.reshape(-1)).to(dev)
+    d_buf = torch.full((GUARD + m * n + GUARD,), float(SENTINEL), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    rc = g.gemm_f16_nn_f32_raw(m, n, k, a_buf.data_ptr() + 2 * a_offset, b_buf.data_ptr() + 2 * b_offset,
+                               d_buf.data_ptr() + 4 * GUARD, stream.cuda_stream, **opts)
+    assert rc == g.OK, g.status_string(rc)
+    torch.cuda.synchronize()
+    host = d_buf.cpu().numpy()
+    assert np.all(host[:GUARD] == SENTINEL) and np.all(host[GUARD + m * n:] == SENTINEL), "write outside D"
+    return host[GUARD:GUARD + m * n].reshape(m, n)
+
+
+def assert_exact(got, ref64, what):
+    bad = np.argwhere(got.astype(np.float64) != ref64)
+    assert bad.size == 0, (f"{what}: {len(bad)} mismatches, first at {tuple(bad[0])}: "
+                           f"gpu {got[tuple(bad[0])]} ref {ref64[tuple(bad[0])]}")
+
+
+def assert_fp32_bound(got, ref64, dabs, k, what):
+    u = 2.0 ** -24
+    gamma = k * u / (1 - k * u)
+    err = np.abs(got.astype(np.float64) - ref64)
+    tol = 2.0 * gamma * dabs + 1e-30
+    ratio = err / tol
+    idx = np.unravel_index(int(np.argmax(ratio)), ratio.shape)
+    assert np.all(err <= tol), f"{what}: worst err/bound {ratio[idx]:.3f} at {idx}"
+    ok, worst, widx = pins.check_rel(got, ref64, 1e-3)
+    assert ok, f"{what}: day-78 gate rel {worst} at {widx}"
+
+
+@pytest.mark.parametrize("name", ["gemm_nn_256_eighths", "gemm_nn_5000x3000x1000_eighths"])
+def test_day78_workloads_exact(name):
+    _announce(name)
+    a, b = inputs.workload_inputs(name)
+    got = run_nn(a, b)
+    d64, _ = oracle.gemm_f16_nn_f64(a, b)
+    assert_exact(got, d64, name)
+    ok, worst, idx = pins.check_rel(got, d64, 1e-3)
+    assert ok, f"rel {worst} at {idx}"
+
+
+@pytest.mark.parametrize("tile", NN_TILES)
+def test_identity_and_one_hot(tile):
+    """A = I => D = B; one-hot rows of A select rows of B: pins the transposed
+    B fragment reads and the fp32 result layout for every tile."""
+    _announce("nn identity/one-hot", tile)
+    rng = np.random.default_rng(60 + tile)
+    k, n = 192, 264
+    b = rng.standard_normal((k, n)).astype(np.float16)
+    assert_exact(run_nn(np.eye(k, dtype=np.float16), b, tile=tile), b.astype(np.float64), "A = I")
+    m = 300
+    p = rng.integers(0, k, size=m)
+    a = np.zeros((m, k), dtype=np.float16)
+    a[np.arange(m), p] = 1.0
+    assert_exact(run_nn(a, b, tile=tile), b[p].astype(np.float64), "one-hot")
+
+
+RAGGED = [(1, 8, 8), (7, 16, 3), (31, 40, 17), (65, 72, 64), (129, 200, 136), (255, 264, 1000),
+          (300, 72, 7), (513, 136, 65)]
+
+
+@pytest.mark.parametrize("m,n,k", RAGGED)
+@pytest.mark.parametrize("tile", NN_TILES)
+def test_ragged_shapes(m, n, k, tile):
+    _announce("nn ragged", m, n, k, tile)
+    rng = np.random.default_rng(m * 3 + n * 5 + k)
+    a = rng.standard_normal((m, k)).astype(np.float16)
+    b = rng.standard_normal((k, n)).astype(np.float16)
+    d64, dabs = oracle.gemm_f16_nn_f64(a, b)
+    assert_fp32_bound(run_nn(a, b, tile=tile), d64, dabs, k, f"{m}x{n}x{k}")
+
+
+@pytest.mark.parametrize("m,n,k", [(70, 13, 40), (33, 100, 24), (64, 21, 19)])
+def test_n_or_k_not_multiple_of_8_takes_the_scalar_loaders(m, n, k):
+    _announce("nn scalar", m, n, k)
+    rng = np.random.default_rng(n * k)
+    a = (rng.integers(-8, 9, size=(m, k)) / 8).astype(np.float16)
+    b = (rng.integers(-8, 9, size=(k, n)) / 8).astype(np.float16)
+    d64, _ = oracle.gemm_f16_nn_f64(a, b)
+    assert_exact(run_nn(a, b), d64, "scalar path")
+    assert_exact(run_nn(a, b, a_offset=1, b_offset=3), d64, "unaligned")
+
+
+def test_k_zero_and_empty():
+    _announce("nn degenerate")
+    got = run_nn(np.zeros((9, 0), np.float16), np.zeros((0, 12), np.float16))
+    assert np.all(got == 0) and not np.any(np.signbit(got))
+    assert run_nn(np.zeros((0, 8), np.float16), np.ones((8, 16), np.float16)).shape == (0, 16)
+
+
+def test_8192_uniform_sampled_rows():
+    """The measurement workload of this contract, default launch; the oracle
+    computes one row per 256-row block tile."""
+    _announce("gemm_nn_8192_uniform")
+    w = inputs.WORKLOADS["gemm_nn_8192_uniform"]
+    a, b = inputs.workload_inputs(w.name)
+    got = run_nn(a, b)
+    rows = sorted({0, w.m - 1} | {t * 256 + (t * 53 + 7) % 256 for t in range(w.m // 256)})
+    d64, dabs = oracle.gemm_f16_nn_f64(a, b, rows=rows)
+    assert_fp32_bound(got[rows], d64, dabs, w.k, w.name)
+
+
+def test_schedule_options_do_not_change_bits():
+    _announce("nn determinism")
+    rng = np.random.default_rng(77)
+    a = rng.standard_normal((1024, 384)).astype(np.float16)
+    b = rng.standard_normal((384, 1280)).astype(np.float16)
+    base = run_nn(a, b, tile=g.TILE_256x256)
+    for sw, xcd in [(1, 0), (3, 1), (8, 0)]:
+        assert np.array_equal(run_nn(a, b, tile=g.TILE_256x256, swizzle=sw, xcd=xcd).view(np.uint32),
+                              base.view(np.uint32))
+
+
+def test_torch_wrapper():
+    _announce("nn torch wrapper")
+    rng = np.random.default_rng(4)
+    a = rng.standard_normal((200, 96)).astype(np.float16)
+    b = rng.standard_normal((96, 136)).astype(np.float16)
+    d = g.gemm_f16_nn_f32(torch.from_numpy(a).cuda(), torch.from_numpy(b).cuda())
+    torch.cuda.synchronize()
+    d64, dabs = oracle.gemm_f16_nn_f64(a, b)
+    assert_fp32_bound(d.cpu().numpy(), d64, dabs, 96, "wrapper")
