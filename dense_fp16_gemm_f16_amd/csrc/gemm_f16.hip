@@ -111,11 +111,18 @@ struct Cfg {
 // write on gfx950, measured with SQ_LDS_BANK_CONFLICT).
 __device__ __forceinline__ int half_swap(int row) { return ((row >> 2) ^ (row >> 3)) & 1; }
 
+// Buffer descriptor (base, num_records).  Both are wave-uniform by
+// construction; readfirstlane states it, so the descriptor lives in SGPRs
+// and the loads need no per-lane loop over distinct descriptors.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *base, uint32_t bytes) {
+    const uint64_t addr = (uint64_t)(uintptr_t)base;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)addr);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(addr >> 32));
+    const uint32_t n = __builtin_amdgcn_readfirstlane(bytes);
+    void *b = (void *)(uintptr_t)(((uint64_t)hi << 32) | lo);
     // word3 0x00020000: raw (untyped) 32-bit data format, as gfx9-family
     // buffer descriptors expect.
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(base), (short)0, (int)bytes,
-                                             0x00020000);
+    return __builtin_amdgcn_make_buffer_rsrc(b, (short)0, (int)n, 0x00020000);
 }
 
 // LDS barrier that waits only for this wave's LDS traffic (lgkmcnt), not for
