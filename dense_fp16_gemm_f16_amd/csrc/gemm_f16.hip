@@ -11,7 +11,9 @@
 //  * loader     buffer_load_dwordx4 of 16-byte K-chunks (one 128-byte row
 //               segment per 8 lanes), staged in VGPRs one K-tile ahead and
 //               written to a 2-stage LDS ring.  Buffer descriptors bound
-//               each operand tile, so rows past M / N read as zero;
+//               each operand tile, so rows past M / N read as zero; when K
+//               is a multiple of the K-tile one descriptor serves the whole
+//               K walk and the K-tile offset rides in the scalar offset;
 //  * LDS        a stage holds each operand as four 16-wide k planes of
 //               32-byte rows; within a row the two 16-byte halves swap by
 //               a bit of the row index and planes are padded, so both the
@@ -22,8 +24,10 @@
 //               as independent 32x32 fp32 accumulators fed by
 //               v_mfma_f32_32x32x16_f16; fragment reads run one 16-wide k
 //               step ahead of the MFMAs that use them;
-//  * epilogue   fp32 -> fp16 round-to-nearest-even, stores masked to
-//               [M, N].
+//  * epilogue   fp32 -> fp16 round-to-nearest-even (or the fp32 value
+//               itself), each wave's piece of C staged through LDS so that
+//               16 consecutive lanes store one contiguous row segment;
+//               stores masked to [M, N].
 //
 // The sum of each output runs over K-tiles in increasing order, and inside
 // a K-tile over 16-wide k steps in increasing order, whatever the grid
@@ -76,7 +80,6 @@ struct Params {
     int32_t k_tiles;       // ceil(k / BK)
     int32_t swizzle;
     int32_t xcd;
-    int32_t vec_c;         // rows of C allow 4-element vector stores (N % 4 == 0, aligned base)
 };
 
 // Block-tile configuration: BM x BN output tile, K walked 64 at a time in
@@ -152,7 +155,7 @@ __device__ __forceinline__ void lds_barrier() {
 // K-tile (ROWS x 64 fp16 = ROWS x 8 chunks of 16 bytes); thread t owns
 // chunk t % 8 of rows t / 8 + RPP * i, so every 8 consecutive lanes read one
 // 128-byte row segment.
-template <class C, int ROWS, int WROWS, bool VEC>
+template <class C, int ROWS, int WROWS, bool VEC, bool KFULL>
 struct KMajorOperand {
     static constexpr int RPP = C::kRowsPerPass;
     static constexpr int kPasses = ROWS / RPP;
@@ -171,8 +174,9 @@ struct KMajorOperand {
     int chunk, row0, k_elems, k_tiles;
     const _Float16 *tile;
     uint32_t bytes;
-    __amdgpu_buffer_rsrc_t rsrc0, rsrc_t;
+    __amdgpu_buffer_rsrc_t rsrc0, rsrc_t, rsrc_none;
     uint32_t mask;
+    uint32_t soff;  // KFULL: byte offset of the K-tile inside each row
     int k0;
     int w_lane, r_lane;
 
@@ -188,6 +192,7 @@ struct KMajorOperand {
         tile = base;
         bytes = (uint32_t)rows_valid * (uint32_t)K * 2u;
         rsrc0 = make_rsrc(base, bytes);
+        rsrc_none = make_rsrc(base, 0u);
 #pragma unroll
         for (int i = 0; i < kPasses; ++i) voff[i] = (uint32_t)((row0 + RPP * i) * K + chunk * 8) * 2u;
         w_lane = lds + (chunk >> 1) * kPlane + row0 * 32 + (((chunk & 1) ^ half_swap(row0)) * 16);
@@ -200,19 +205,33 @@ struct KMajorOperand {
         r_lane = lds + fplane * kPlane + (frag_row + frow) * 32 + ((fhalf ^ half_swap(frow)) * 16);
     }
 
-    // Chunks past K (K % 8 == 0 on the VEC path, so a chunk is wholly inside
-    // or wholly past K) get kOutOfRange and read as zero.
+    // KFULL (K % BK == 0, VEC): the block's descriptor for every K-tile,
+    // the K-tile's byte offset in soffset, and an empty descriptor for the
+    // K-tiles past K.  Otherwise a descriptor per K-tile whose range ends
+    // with the block's last row; chunks past K (K % 8 == 0 on the VEC path,
+    // so a chunk is wholly inside or wholly past K) get kOutOfRange.  Both
+    // read zeros wherever the tile leaves the matrix.
     __device__ __forceinline__ void begin_tile(int t) {
-        const uint32_t skip = (uint32_t)t * (C::BK * 2);
-        const bool live = t < k_tiles;
-        rsrc_t = make_rsrc(tile + (live ? t * C::BK : 0), (live && bytes > skip) ? bytes - skip : 0u);
         k0 = t * C::BK;
-        mask = (k0 + chunk * 8 >= k_elems) ? kOutOfRange : 0u;
+        if constexpr (VEC && KFULL) {
+            rsrc_t = t < k_tiles ? rsrc0 : rsrc_none;
+            soff = (uint32_t)k0 * 2u;
+            mask = 0;
+        } else {
+            const uint32_t skip = (uint32_t)t * (C::BK * 2);
+            const bool live = t < k_tiles;
+            rsrc_t = make_rsrc(tile + (live ? t * C::BK : 0), (live && bytes > skip) ? bytes - skip : 0u);
+            soff = 0;
+            mask = (k0 + chunk * 8 >= k_elems) ? kOutOfRange : 0u;
+        }
     }
 
     __device__ __forceinline__ void load(int i) {
         if constexpr (VEC) {
-            regs[i] = __builtin_amdgcn_raw_buffer_load_b128(rsrc_t, voff[i] | mask, 0, 0);
+            if constexpr (KFULL)
+                regs[i] = __builtin_amdgcn_raw_buffer_load_b128(rsrc_t, voff[i], soff, 0);
+            else
+                regs[i] = __builtin_amdgcn_raw_buffer_load_b128(rsrc_t, voff[i] | mask, 0, 0);
         } else {
             // every element bounds-checked against K; rows past the tile's
             // valid rows are past num_records
@@ -344,14 +363,15 @@ struct NMajorB {
 //
 // NN == false: C fp16 [M,N] = A [M,K] * B[N,K]^T (the tutorial's contract).
 // NN == true:  D fp32 [M,N] = A [M,K] * B[K,N]   (the day-78 listing's).
-template <class C, bool VEC, bool NN>
+// KFULL: VEC and K a multiple of the K-tile (one descriptor per operand).
+template <class C, bool VEC, bool NN, bool KFULL>
 __global__ __launch_bounds__(C::kThreads)
 __attribute__((amdgpu_waves_per_eu(C::kMinWavesPerEU, C::kMinWavesPerEU)))
 void gemm_f16_kernel(const Params p) {
     constexpr int BM = C::BM, BN = C::BN, KS = C::KS;
     constexpr int TM = C::TM, TN = C::TN, FM = C::FM, FN = C::FN, MB = C::MB;
-    using OpA = KMajorOperand<C, BM, TM, VEC>;
-    using OpB = std::conditional_t<NN, NMajorB<C, VEC>, KMajorOperand<C, BN, TN, VEC>>;
+    using OpA = KMajorOperand<C, BM, TM, VEC, KFULL>;
+    using OpB = std::conditional_t<NN, NMajorB<C, VEC>, KMajorOperand<C, BN, TN, VEC, KFULL>>;
     constexpr int PA = OpA::kPasses, PB = OpB::kPasses;
     constexpr int kLdsB = OpA::kLdsBytes;
     static_assert(OpA::kLdsBytes + OpB::kLdsBytes <= 160 * 1024, "LDS budget");
@@ -507,44 +527,73 @@ void gemm_f16_kernel(const Params p) {
     // holds row 8*(r/4) + 4*(l/32) + r%4, column l%32; for 16x16 blocks,
     // row 4*(l/16) + r, column l%16.  With the swapped operands the row is n
     // and the column is m, so each group of 4 registers is 4 consecutive n.
+    using Out = std::conditional_t<NN, float, _Float16>;
+    using Out4 = std::conditional_t<NN, floatx4, half4>;
+    constexpr int ES = (int)sizeof(Out);
     constexpr int kGroups = MB == 32 ? 4 : 1;
     const int frow = lane % MB;
     const int quad = MB == 32 ? (lane >> 5) * 4 : (lane >> 4) * 4;
+    auto out4 = [&](int j, int i, int g) {
+        Out4 o;
 #pragma unroll
-    for (int i = 0; i < FM; ++i) {
-        const int m = m0 + wm * TM + i * MB + frow;
-        if (m >= p.m) continue;
+        for (int e = 0; e < 4; ++e) o[e] = (Out)acc[j][i][4 * g + e];  // fp16: round to nearest even
+        return o;
+    };
+
+    // Each wave's TM x TN piece goes through LDS in passes of SR rows: row r
+    // of a pass holds TN outputs (CPR chunks of 16 bytes, chunk c at slot
+    // c ^ (r % CPR)); then lane l of a store moves chunk l % CPR of row
+    // l / CPR, so CPR consecutive lanes write one contiguous row segment.
+    constexpr int RB = TN * ES, CPR = RB / 16;
+    constexpr int kLds = OpA::kLdsBytes + OpB::kLdsBytes;
+    constexpr int SR = C::kWaves * TM * RB <= kLds         ? TM
+                       : C::kWaves * (TM / 2) * RB <= kLds ? TM / 2
+                                                            : TM / 4;
+    static_assert(C::kWaves * SR * RB <= kLds && SR % MB == 0 && (SR * CPR) % kWave == 0, "staging");
+    char *const stg = smem + wave * (SR * RB);
+    lds_barrier();  // every wave is done with the operand stages
+    // an opaque zero keeps the staging addresses from being computed before
+    // the K loop, where they would only hold registers
+    int lz;
+    asm volatile("v_mov_b32 %0, 0" : "=v"(lz));
+    const int erow = frow + lz;
+    const bool vec16 = (p.n % (16 / ES)) == 0 && ((uintptr_t)p.c % 16) == 0;
 #pragma unroll
-        for (int j = 0; j < FN; ++j) {
+    for (int pass = 0; pass < TM / SR; ++pass) {
 #pragma unroll
-            for (int g = 0; g < kGroups; ++g) {
-                const int n = n0 + wn * TN + j * MB + 8 * g + quad;
-                if constexpr (NN) {
-                    // fp32 out: the accumulator itself, unrounded
-                    float *drow = static_cast<float *>(p.c) + (int64_t)m * p.n;
-                    const floatx4 v = {acc[j][i][4 * g + 0], acc[j][i][4 * g + 1], acc[j][i][4 * g + 2],
-                                       acc[j][i][4 * g + 3]};
-                    if (p.vec_c && n + 3 < p.n) {
-                        *reinterpret_cast<floatx4 *>(drow + n) = v;
-                    } else {
+        for (int i = pass * (SR / MB); i < (pass + 1) * (SR / MB); ++i) {
+            const int rl = (i - pass * (SR / MB)) * MB + erow;
 #pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            if (n + e < p.n) drow[n + e] = v[e];
-                    }
+            for (int j = 0; j < FN; ++j) {
+#pragma unroll
+                for (int g = 0; g < kGroups; ++g) {
+                    const int byte = (j * MB + 8 * g + quad) * ES;
+                    *reinterpret_cast<Out4 *>(stg + rl * RB + (((byte >> 4) ^ (rl % CPR)) << 4) + (byte & 15)) =
+                        out4(j, i, g);
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+#pragma unroll
+        for (int s = 0; s < SR * CPR / kWave; ++s) {
+            const int idx = s * kWave + lane;
+            const int r = idx / CPR, c = idx % CPR;
+            const int4v v = *reinterpret_cast<const int4v *>(stg + r * RB + ((c ^ (r % CPR)) << 4));
+            const int m = m0 + wm * TM + pass * SR + r;
+            const int n = n0 + wn * TN + c * (16 / ES);
+            if (m < p.m) {
+                Out *crow = static_cast<Out *>(p.c) + (int64_t)m * p.n;
+                if (vec16 && n + 16 / ES - 1 < p.n) {
+                    *reinterpret_cast<int4v *>(crow + n) = v;
                 } else {
-                    _Float16 *crow = static_cast<_Float16 *>(p.c) + (int64_t)m * p.n;
-                    half4 h;
-                    h[0] = (_Float16)acc[j][i][4 * g + 0];
-                    h[1] = (_Float16)acc[j][i][4 * g + 1];
-                    h[2] = (_Float16)acc[j][i][4 * g + 2];
-                    h[3] = (_Float16)acc[j][i][4 * g + 3];
-                    if (p.vec_c && n + 3 < p.n) {
-                        *reinterpret_cast<half4 *>(crow + n) = h;
-                    } else {
+                    union {
+                        int4v v;
+                        Out e[16 / ES];
+                    } u;
+                    u.v = v;
 #pragma unroll
-                        for (int e = 0; e < 4; ++e)
-                            if (n + e < p.n) crow[n + e] = h[e];
-                    }
+                    for (int e = 0; e < 16 / ES; ++e)
+                        if (n + e < p.n) crow[n + e] = u.e[e];
                 }
             }
         }
@@ -654,10 +703,12 @@ static int check_device() {
 template <class C, bool NN>
 static void launch(const Params &p, bool vec, hipStream_t stream) {
     const dim3 grid((unsigned)((int64_t)p.num_m * p.num_n));
-    if (vec)
-        hipLaunchKernelGGL((gemm_f16_kernel<C, true, NN>), grid, dim3(C::kThreads), 0, stream, p);
+    if (vec && p.k % C::BK == 0)
+        hipLaunchKernelGGL((gemm_f16_kernel<C, true, NN, true>), grid, dim3(C::kThreads), 0, stream, p);
+    else if (vec)
+        hipLaunchKernelGGL((gemm_f16_kernel<C, true, NN, false>), grid, dim3(C::kThreads), 0, stream, p);
     else
-        hipLaunchKernelGGL((gemm_f16_kernel<C, false, NN>), grid, dim3(C::kThreads), 0, stream, p);
+        hipLaunchKernelGGL((gemm_f16_kernel<C, false, NN, false>), grid, dim3(C::kThreads), 0, stream, p);
 }
 
 template <bool NN>
@@ -719,8 +770,6 @@ static int gemm_impl(bool nn, int64_t m, int64_t n, int64_t k, const void *a, co
     p.k_tiles = (int32_t)cdiv(k, 64);
     p.swizzle = o.swizzle ? o.swizzle : 4;
     p.xcd = o.xcd < 0 ? 1 : o.xcd;
-    // 4-element vector stores: 8 bytes (fp16) or 16 bytes (fp32)
-    p.vec_c = ((n % 4) == 0 && ((uintptr_t)c % (4 * out_bytes)) == 0) ? 1 : 0;
     // 16-byte loads need 16-byte aligned rows of A, and of B in its layout
     const bool vec = (k % 8) == 0 && (!nn || (n % 8) == 0) && ((uintptr_t)a % 16) == 0 &&
                      ((uintptr_t)b % 16) == 0;
