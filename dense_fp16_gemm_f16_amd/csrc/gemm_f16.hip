@@ -70,6 +70,15 @@ constexpr uint32_t kOutOfRange = 0x80000000u;  // buffer offset past any num_rec
 #ifndef GEMM_PLANE_PAD
 #define GEMM_PLANE_PAD 32
 #endif
+// MFMA of the last k step after which the K-tile's workgroup barrier sits
+// (a few MFMAs in, the wave's last fragment reads of the stage are done)
+#ifndef GEMM_BAR_MFMA
+#define GEMM_BAR_MFMA 2
+#endif
+// staging register sets (1 or 2; a second set prefetches one more K-tile)
+#ifndef GEMM_STAGE_SETS
+#define GEMM_STAGE_SETS 1
+#endif
 
 struct Params {
     const _Float16 *a;
@@ -100,6 +109,11 @@ struct Cfg {
     static constexpr int FM = TM / MB, FN = TN / MB;
     static constexpr int kRowsPerPass = kThreads / 8;  // 8 chunks of 16 B per 64-wide row
     static constexpr int kMinWavesPerEU = kWaves <= 4 ? 1 : kWaves / 4;
+    // staging register sets: with two, the loads of a K-tile are issued two
+    // K-tiles before it is written to LDS.  Measured on gfx950 a second set
+    // buys nothing (the loads are throughput-, not latency-bound), so the
+    // default is one.
+    static constexpr int kSets = GEMM_STAGE_SETS;
     static_assert(MB == 32 || MB == 16, "MFMA block edge");
     static_assert(TM % MB == 0 && TN % MB == 0, "wave tile must be whole MFMA blocks");
     static_assert(kRowsPerPass % 32 == 0, "passes must keep row bits 2-4 per lane");
@@ -155,7 +169,7 @@ __device__ __forceinline__ void lds_barrier() {
 // K-tile (ROWS x 64 fp16 = ROWS x 8 chunks of 16 bytes); thread t owns
 // chunk t % 8 of rows t / 8 + RPP * i, so every 8 consecutive lanes read one
 // 128-byte row segment.
-template <class C, int ROWS, int WROWS, bool VEC, bool KFULL>
+template <class C, int ROWS, int WROWS, bool VEC, bool KFULL, int SETS>
 struct KMajorOperand {
     static constexpr int RPP = C::kRowsPerPass;
     static constexpr int kPasses = ROWS / RPP;
@@ -169,7 +183,7 @@ struct KMajorOperand {
     static_assert(kStage + (C::kPlanes - 1) * kPlane + (WROWS - C::MB) * 32 < 65536,
                   "LDS immediates must fit the 16-bit offset field");
 
-    int4v regs[kPasses];
+    int4v regs[SETS][kPasses];
     uint32_t voff[kPasses];  // VEC: byte offset of this lane's chunk from the K-tile start
     int chunk, row0, k_elems, k_tiles;
     const _Float16 *tile;
@@ -226,12 +240,12 @@ struct KMajorOperand {
         }
     }
 
-    __device__ __forceinline__ void load(int i) {
+    __device__ __forceinline__ void load(int i, int set) {
         if constexpr (VEC) {
             if constexpr (KFULL)
-                regs[i] = __builtin_amdgcn_raw_buffer_load_b128(rsrc_t, voff[i], soff, 0);
+                regs[set][i] = __builtin_amdgcn_raw_buffer_load_b128(rsrc_t, voff[i], soff, 0);
             else
-                regs[i] = __builtin_amdgcn_raw_buffer_load_b128(rsrc_t, voff[i] | mask, 0, 0);
+                regs[set][i] = __builtin_amdgcn_raw_buffer_load_b128(rsrc_t, voff[i] | mask, 0, 0);
         } else {
             // every element bounds-checked against K; rows past the tile's
             // valid rows are past num_records
@@ -247,12 +261,12 @@ struct KMajorOperand {
                     (kc + e < k_elems) ? (uint32_t)(row * k_elems + kc + e) * 2u : kOutOfRange;
                 u.s[e] = __builtin_amdgcn_raw_buffer_load_b16(rsrc0, off, 0, 0);
             }
-            regs[i] = u.v;
+            regs[set][i] = u.v;
         }
     }
 
-    __device__ __forceinline__ void store(char *smem, int i, int stage) const {
-        *reinterpret_cast<int4v *>(smem + w_lane + stage * kStage + i * RPP * 32) = regs[i];
+    __device__ __forceinline__ void store(char *smem, int i, int stage, int set) const {
+        *reinterpret_cast<int4v *>(smem + w_lane + stage * kStage + i * RPP * 32) = regs[set][i];
     }
 
     __device__ __forceinline__ half8 read(const char *smem, int stage, int ks, int f) const {
@@ -271,7 +285,7 @@ struct KMajorOperand {
 // half-wave fall on disjoint banks.  Each pass covers RPP k-rows; thread t
 // owns 16-byte chunk t % (BN/8) of k-row t / (BN/8) + RPP * i, so
 // consecutive lanes read consecutive n (coalesced).
-template <class C, bool VEC>
+template <class C, bool VEC, int SETS>
 struct NMajorB {
     static constexpr int BN = C::BN, BK = C::BK;
     static constexpr int kCpr = BN / 8;  // 16-byte chunks per k-row
@@ -284,7 +298,7 @@ struct NMajorB {
     static_assert(C::kThreads % kCpr == 0 && BK % RPP == 0, "loader passes");
     static_assert(15 * kPitch + 4 * kPitch + BN * 2 < 65536, "LDS immediates");
 
-    int4v regs[kPasses];
+    int4v regs[SETS][kPasses];
     uint32_t voff[kPasses];  // VEC: byte offset from the K-tile's first row; bit 31 set past N
     int chunk, row0, n_total, k_elems, k_tiles, n0;
     const _Float16 *b;
@@ -319,9 +333,9 @@ struct NMajorB {
         rsrc_t = make_rsrc(b + (t < k_tiles ? (int64_t)k0 * n_total : 0), (uint32_t)rows * (uint32_t)n_total * 2u);
     }
 
-    __device__ __forceinline__ void load(int i) {
+    __device__ __forceinline__ void load(int i, int set) {
         if constexpr (VEC) {
-            regs[i] = __builtin_amdgcn_raw_buffer_load_b128(rsrc_t, voff[i], 0, 0);
+            regs[set][i] = __builtin_amdgcn_raw_buffer_load_b128(rsrc_t, voff[i], 0, 0);
         } else {
             const int row = row0 + RPP * i;
             const int nc = n0 + chunk * 8;
@@ -334,12 +348,12 @@ struct NMajorB {
                 const uint32_t off = (nc + e < n_total) ? (uint32_t)(row * n_total + nc + e) * 2u : kOutOfRange;
                 u.s[e] = __builtin_amdgcn_raw_buffer_load_b16(rsrc_t, off, 0, 0);
             }
-            regs[i] = u.v;
+            regs[set][i] = u.v;
         }
     }
 
-    __device__ __forceinline__ void store(char *smem, int i, int stage) const {
-        *reinterpret_cast<int4v *>(smem + w_lane + stage * kStage + i * RPP * kPitch) = regs[i];
+    __device__ __forceinline__ void store(char *smem, int i, int stage, int set) const {
+        *reinterpret_cast<int4v *>(smem + w_lane + stage * kStage + i * RPP * kPitch) = regs[set][i];
     }
 
     __device__ __forceinline__ half8 read(const char *smem, int stage, int ks, int f) const {
@@ -359,171 +373,14 @@ struct NMajorB {
     }
 };
 
-// ---- the kernel -----------------------------------------------------------
-//
-// NN == false: C fp16 [M,N] = A [M,K] * B[N,K]^T (the tutorial's contract).
-// NN == true:  D fp32 [M,N] = A [M,K] * B[K,N]   (the day-78 listing's).
-// KFULL: VEC and K a multiple of the K-tile (one descriptor per operand).
-template <class C, bool VEC, bool NN, bool KFULL>
-__global__ __launch_bounds__(C::kThreads)
-__attribute__((amdgpu_waves_per_eu(C::kMinWavesPerEU, C::kMinWavesPerEU)))
-void gemm_f16_kernel(const Params p) {
-    constexpr int BM = C::BM, BN = C::BN, KS = C::KS;
-    constexpr int TM = C::TM, TN = C::TN, FM = C::FM, FN = C::FN, MB = C::MB;
-    using OpA = KMajorOperand<C, BM, TM, VEC, KFULL>;
-    using OpB = std::conditional_t<NN, NMajorB<C, VEC>, KMajorOperand<C, BN, TN, VEC, KFULL>>;
-    constexpr int PA = OpA::kPasses, PB = OpB::kPasses;
-    constexpr int kLdsB = OpA::kLdsBytes;
-    static_assert(OpA::kLdsBytes + OpB::kLdsBytes <= 160 * 1024, "LDS budget");
-    __shared__ __attribute__((aligned(1024))) char smem[OpA::kLdsBytes + OpB::kLdsBytes];
-
-    const int tid = threadIdx.x;
-    const int lane = tid & (kWave - 1);
-    const int wave = tid / kWave;
-    const int wm = wave / C::WN;
-    const int wn = wave % C::WN;
-
-    const TileCoord tc = tile_coord(blockIdx.x, p.num_m, p.num_n, p.swizzle, p.xcd != 0);
-    const int m0 = (int)tc.m_block * BM;
-    const int n0 = (int)tc.n_block * BN;
-    const int kt_count = p.k_tiles;
-    if (kt_count == 0) return;  // never launched with K == 0
-
-    // Per-tile buffer descriptors: rows past M (N) lie beyond num_records.
-    OpA opa;
-    OpB opb;
-    opa.init(p.a + (int64_t)m0 * p.k, min(BM, p.m - m0), p.k, kt_count, tid, lane, wm * TM, 0);
-    if constexpr (NN)
-        opb.init(p.b, n0, p.n, p.k, kt_count, tid, lane, wn * TN, kLdsB);
-    else
-        opb.init(p.b + (int64_t)n0 * p.k, min(BN, p.n - n0), p.k, kt_count, tid, lane, wn * TN, kLdsB);
-
-    using M = Mfma<MB>;
-    typename M::Acc acc[FN][FM];
-#pragma unroll
-    for (int j = 0; j < FN; ++j)
-#pragma unroll
-        for (int i = 0; i < FM; ++i) acc[j][i] = typename M::Acc{};
-
-    half8 af[2][FM];
-    half8 bf[2][FN];
-    auto read_frags = [&](int buf, int stage, int ks) {
-        // in the order the MFMAs consume them: B0, A0..A(FM-1), B1..
-        bf[buf][0] = opb.read(smem, stage, ks, 0);
-#pragma unroll
-        for (int i = 0; i < FM; ++i) af[buf][i] = opa.read(smem, stage, ks, i);
-#pragma unroll
-        for (int j = 1; j < FN; ++j) bf[buf][j] = opb.read(smem, stage, ks, j);
-    };
-
-    // Prologue: K-tile 0 into stage 0, K-tile 1 (zeros if K has one K-tile)
-    // into the staging registers.
-    opa.begin_tile(0);
-    opb.begin_tile(0);
-#pragma unroll
-    for (int i = 0; i < PA; ++i) opa.load(i);
-#pragma unroll
-    for (int i = 0; i < PB; ++i) opb.load(i);
-#pragma unroll
-    for (int i = 0; i < PA; ++i) opa.store(smem, i, 0);
-#pragma unroll
-    for (int i = 0; i < PB; ++i) opb.store(smem, i, 0);
-    opa.begin_tile(1);
-    opb.begin_tile(1);
-#pragma unroll
-    for (int i = 0; i < PA; ++i) opa.load(i);
-#pragma unroll
-    for (int i = 0; i < PB; ++i) opb.load(i);
-    lds_barrier();
-    read_frags(0, 0, 0);
-
-    // One K-tile of work, as KS k steps (MK wide) on stage STAGE, which also
-    // moves the staged K-tile kt+1 into the other stage and refills the
-    // staging registers with K-tile kt+2.  Past the last K-tile those moves
-    // carry zeros that are never read, so every iteration is the same
-    // branch-free block, whose issue order is pinned:
-    //   step ks < KS-1: MFMAs of step ks interleaved with the fragment reads
-    //                   for step ks+1 and a slice of the LDS writes and
-    //                   global loads;
-    //   step KS-1:      wait for this wave's LDS traffic, workgroup barrier,
-    //                   then MFMAs of step KS-1 interleaved with the
-    //                   fragment reads for step 0 of K-tile kt+1.
-    constexpr int kSlices = KS - 1;
-    auto k_iter = [&](auto stage_tag, int kt) {
-        constexpr int STAGE = decltype(stage_tag)::value;
-        constexpr int NXT = STAGE ^ 1;
-        opa.begin_tile(kt + 2);
-        opb.begin_tile(kt + 2);
-#pragma unroll
-        for (int ks = 0; ks < KS; ++ks) {
-            const int cur = ks & 1;
-            constexpr int NM = FM * FN;
-            if (ks + 1 < KS) {
-                read_frags(cur ^ 1, STAGE, ks + 1);
-            } else {
-                // The other stage is complete for everyone, and everyone has
-                // read its last fragments of this stage.
-                lds_barrier();
-                read_frags(cur ^ 1, NXT, 0);
-            }
-            if (ks < kSlices) {
-#pragma unroll
-                for (int i = ks * PA / kSlices; i < (ks + 1) * PA / kSlices; ++i) {
-                    opa.store(smem, i, NXT);
-                    opa.load(i);
-                }
-#pragma unroll
-                for (int i = ks * PB / kSlices; i < (ks + 1) * PB / kSlices; ++i) {
-                    opb.store(smem, i, NXT);
-                    opb.load(i);
-                }
-            }
-            // B fragments feed the MFMA's A operand and A fragments its B
-            // operand, so each result block is C^T: a lane then holds 4
-            // consecutive n of one m row, which store as one vector.
-#pragma unroll
-            for (int j = 0; j < FN; ++j)
-#pragma unroll
-                for (int i = 0; i < FM; ++i) acc[j][i] = M::run(bf[cur][j], af[cur][i], acc[j][i]);
-            // Pin the issue order: after each MFMA, an even share of this
-            // step's other memory instructions (fragment reads first, then
-            // LDS write / global load pairs).
-            {
-                const int nr = NN ? FM + 2 * FN : FM + FN;
-                const int nw = ks < kSlices ? ((ks + 1) * PA / kSlices - ks * PA / kSlices) +
-                                                  ((ks + 1) * PB / kSlices - ks * PB / kSlices)
-                                            : 0;
-                const int total = nr + 2 * nw;
-#pragma unroll
-                for (int m = 0; m < NM; ++m) {
-                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-#pragma unroll
-                    for (int o = m * total / NM; o < (m + 1) * total / NM; ++o) {
-                        if (o < nr) {
-                            __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // DS read
-                        } else if (((o - nr) & 1) == 0) {
-                            __builtin_amdgcn_sched_group_barrier(0x200, 1, 0);  // DS write
-                        } else {
-                            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // VMEM read
-                        }
-                    }
-                }
-            }
-            __builtin_amdgcn_sched_barrier(0);
-        }
-    };
-    using S0 = std::integral_constant<int, 0>;
-    using S1 = std::integral_constant<int, 1>;
-    // K-tiles go in pairs (stage 0, stage 1) with no branch between them.
-    // When the count is odd the last pair's second K-tile lies past K: its
-    // stage holds zeros, so its MFMAs add +0 to accumulators that are never
-    // -0 (they start at +0), which leaves every bit unchanged.
-    for (int kt = 0; kt < kt_count; kt += 2) {
-        k_iter(S0{}, kt);
-        k_iter(S1{}, kt + 1);
-    }
-
-    // Epilogue.  MFMA result layout: for 32x32 blocks, lane l register r
+// Epilogue: the accumulators of one wave to C (fp16, rounded to nearest
+// even) or D (fp32).  smem is the workgroup's LDS of kLds bytes, free once
+// every wave is past the K loop.
+template <class C, bool NN, int kLds>
+__device__ __forceinline__ void store_tile(const typename Mfma<C::MB>::Acc (&acc)[C::FN][C::FM], char *smem,
+                                           const Params &p, int m0, int n0, int wm, int wn, int wave, int lane) {
+    constexpr int TM = C::TM, TN = C::TN, FN = C::FN, MB = C::MB;
+    // MFMA result layout: for 32x32 blocks, lane l register r
     // holds row 8*(r/4) + 4*(l/32) + r%4, column l%32; for 16x16 blocks,
     // row 4*(l/16) + r, column l%16.  With the swapped operands the row is n
     // and the column is m, so each group of 4 registers is 4 consecutive n.
@@ -545,7 +402,6 @@ void gemm_f16_kernel(const Params p) {
     // c ^ (r % CPR)); then lane l of a store moves chunk l % CPR of row
     // l / CPR, so CPR consecutive lanes write one contiguous row segment.
     constexpr int RB = TN * ES, CPR = RB / 16;
-    constexpr int kLds = OpA::kLdsBytes + OpB::kLdsBytes;
     constexpr int SR = C::kWaves * TM * RB <= kLds         ? TM
                        : C::kWaves * (TM / 2) * RB <= kLds ? TM / 2
                                                             : TM / 4;
@@ -599,6 +455,228 @@ void gemm_f16_kernel(const Params p) {
         }
     }
 }
+
+// Compile-time loop: f(std::integral_constant<int, I>) for I in [B, E).
+template <int B, int E, class F>
+__device__ __forceinline__ void static_range(F &&f) {
+    if constexpr (B < E) {
+        f(std::integral_constant<int, B>{});
+        static_range<B + 1, E>(f);
+    }
+}
+
+// A k step's memory operations in issue order R0 W0 L0 R1 W1 L1 ... (nr
+// fragment reads R, nw LDS writes W each followed by its global load L);
+// kind 0 = R, 1 = W, 2 = L, and the index within its kind.
+constexpr int step_op_kind(int o, int nr, int nw) {
+    for (int t = 0;; ++t) {
+        if (t < nr) {
+            if (o == 0) return 0;
+            --o;
+        }
+        if (t < nw) {
+            if (o == 0) return 1;
+            if (o == 1) return 2;
+            o -= 2;
+        }
+    }
+}
+constexpr int step_op_index(int o, int nr, int nw) {
+    for (int t = 0;; ++t) {
+        if (t < nr) {
+            if (o == 0) return t;
+            --o;
+        }
+        if (t < nw) {
+            if (o <= 1) return t;
+            o -= 2;
+        }
+    }
+}
+
+// ---- the kernel -----------------------------------------------------------
+//
+// NN == false: C fp16 [M,N] = A [M,K] * B[N,K]^T (the tutorial's contract).
+// NN == true:  D fp32 [M,N] = A [M,K] * B[K,N]   (the day-78 listing's).
+// KFULL: VEC and K a multiple of the K-tile (one descriptor per operand).
+template <class C, bool VEC, bool NN, bool KFULL>
+__global__ __launch_bounds__(C::kThreads)
+__attribute__((amdgpu_waves_per_eu(C::kMinWavesPerEU, C::kMinWavesPerEU)))
+void gemm_f16_kernel(const Params p) {
+    constexpr int BM = C::BM, BN = C::BN, KS = C::KS;
+    constexpr int TM = C::TM, TN = C::TN, FM = C::FM, FN = C::FN, MB = C::MB;
+    // the scalar loader's per-element loads keep too many registers in
+    // flight for a second staging set
+    constexpr int SETS = VEC ? C::kSets : 1;
+    using OpA = KMajorOperand<C, BM, TM, VEC, KFULL, SETS>;
+    using OpB = std::conditional_t<NN, NMajorB<C, VEC, SETS>, KMajorOperand<C, BN, TN, VEC, KFULL, SETS>>;
+    constexpr int PA = OpA::kPasses, PB = OpB::kPasses;
+    constexpr int kLdsB = OpA::kLdsBytes;
+    static_assert(OpA::kLdsBytes + OpB::kLdsBytes <= 160 * 1024, "LDS budget");
+    __shared__ __attribute__((aligned(1024))) char smem[OpA::kLdsBytes + OpB::kLdsBytes];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = tid / kWave;
+    const int wm = wave / C::WN;
+    const int wn = wave % C::WN;
+
+    const TileCoord tc = tile_coord(blockIdx.x, p.num_m, p.num_n, p.swizzle, p.xcd != 0);
+    const int m0 = (int)tc.m_block * BM;
+    const int n0 = (int)tc.n_block * BN;
+    const int kt_count = p.k_tiles;
+    if (kt_count == 0) return;  // never launched with K == 0
+
+    // Per-tile buffer descriptors: rows past M (N) lie beyond num_records.
+    OpA opa;
+    OpB opb;
+    opa.init(p.a + (int64_t)m0 * p.k, min(BM, p.m - m0), p.k, kt_count, tid, lane, wm * TM, 0);
+    if constexpr (NN)
+        opb.init(p.b, n0, p.n, p.k, kt_count, tid, lane, wn * TN, kLdsB);
+    else
+        opb.init(p.b + (int64_t)n0 * p.k, min(BN, p.n - n0), p.k, kt_count, tid, lane, wn * TN, kLdsB);
+
+    using M = Mfma<MB>;
+    typename M::Acc acc[FN][FM];
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int i = 0; i < FM; ++i) acc[j][i] = typename M::Acc{};
+
+    half8 af[2][FM];
+    half8 bf[2][FN];
+    auto read_frags = [&](int buf, int stage, int ks) {
+        // in the order the MFMAs consume them: B0, A0..A(FM-1), B1..
+        bf[buf][0] = opb.read(smem, stage, ks, 0);
+#pragma unroll
+        for (int i = 0; i < FM; ++i) af[buf][i] = opa.read(smem, stage, ks, i);
+#pragma unroll
+        for (int j = 1; j < FN; ++j) bf[buf][j] = opb.read(smem, stage, ks, j);
+    };
+
+    // Prologue: K-tile 0 into stage 0; K-tiles 1 .. SETS (zeros past K) into
+    // the staging register sets, K-tile x in set x % SETS.
+    static_range<0, SETS + 1>([&](auto x_c) {
+        constexpr int x = decltype(x_c)::value;
+        opa.begin_tile(x);
+        opb.begin_tile(x);
+#pragma unroll
+        for (int i = 0; i < PA; ++i) opa.load(i, x % SETS);
+#pragma unroll
+        for (int i = 0; i < PB; ++i) opb.load(i, x % SETS);
+        if constexpr (x == SETS - 1) {
+#pragma unroll
+            for (int i = 0; i < PA; ++i) opa.store(smem, i, 0, 0);
+#pragma unroll
+            for (int i = 0; i < PB; ++i) opb.store(smem, i, 0, 0);
+        }
+    });
+    lds_barrier();
+    read_frags(0, 0, 0);
+
+    // One K-tile of work, as KS k steps (MK wide) on stage STAGE, which also
+    // moves the staged K-tile kt+1 into the other stage and refills its
+    // staging registers with K-tile kt+1+SETS.  Past the last K-tile those moves
+    // carry zeros that are never read, so every iteration is the same
+    // branch-free block.  Its issue order is fixed instruction by
+    // instruction: step ks puts after each of its MFMAs an even share of
+    //   ks < KS-1: the fragment reads for step ks+1 and a slice of the LDS
+    //              writes and global loads, as (read, write, load) triples;
+    //   ks = KS-1: after the first MFMA, a wait for this wave's LDS traffic
+    //              and the workgroup barrier, then the fragment reads for
+    //              step 0 of K-tile kt+1.
+    // LDS writes placed between fragment reads cost almost nothing, where a
+    // run of writes after a run of reads stalls the MFMAs by about ten
+    // cycles per write (measured on gfx950); hence the triples.
+    constexpr int kSlices = KS - 1;
+    constexpr int NM = FM * FN;
+    constexpr int NR = FM + FN;  // fragment reads per step (calls)
+    constexpr int kBarAt = GEMM_BAR_MFMA < NM ? GEMM_BAR_MFMA : NM - 1;
+    auto read_frag = [&](int buf, int stage, int ks, int r) {
+        // in the order the MFMAs consume them: B0, A0..A(FM-1), B1..
+        if (r == 0)
+            bf[buf][0] = opb.read(smem, stage, ks, 0);
+        else if (r <= FM)
+            af[buf][r - 1] = opa.read(smem, stage, ks, r - 1);
+        else
+            bf[buf][r - FM] = opb.read(smem, stage, ks, r - FM);
+    };
+    auto k_iter = [&](auto stage_tag, int kt) {
+        constexpr int STAGE = decltype(stage_tag)::value;
+        constexpr int NXT = STAGE ^ 1;
+        constexpr int SET = SETS == 2 ? NXT : 0;  // (kt + 1) % SETS
+        opa.begin_tile(kt + 1 + SETS);
+        opb.begin_tile(kt + 1 + SETS);
+        static_range<0, KS>([&](auto ks_c) {
+            constexpr int ks = decltype(ks_c)::value;
+            constexpr int cur = ks & 1;
+            constexpr bool last = ks + 1 == KS;
+            constexpr int rstage = last ? NXT : STAGE;
+            constexpr int rks = last ? 0 : ks + 1;
+            constexpr int a0 = ks * PA / kSlices, a1 = last ? a0 : (ks + 1) * PA / kSlices;
+            constexpr int b0 = ks * PB / kSlices, b1 = last ? b0 : (ks + 1) * PB / kSlices;
+            constexpr int nw = (a1 - a0) + (b1 - b0);
+            constexpr int total = NR + 2 * nw;
+            static_range<0, NM>([&](auto m_c) {
+                constexpr int m = decltype(m_c)::value;
+                // B fragments feed the MFMA's A operand and A fragments its
+                // B operand, so each result block is C^T: a lane then holds
+                // 4 consecutive n of one m row, which store as one vector.
+                // snake order: odd rows of blocks run backwards, so each row
+                // starts on the A fragment the previous row ended with (one
+                // operand stays put across every pair of consecutive MFMAs)
+                constexpr int j = m / FM, i = (j & 1) ? FM - 1 - m % FM : m % FM;
+                acc[j][i] = M::run(bf[cur][j], af[cur][i], acc[j][i]);
+                if constexpr (last && m == kBarAt) {
+                    // The other stage is complete for everyone, and everyone
+                    // has read its last fragments of this stage.
+                    lds_barrier();
+                }
+                constexpr int first = last ? kBarAt : 0;  // ops ride after MFMAs first..NM-1
+                constexpr int lo = m < first ? 0 : (m - first) * total / (NM - first);
+                constexpr int hi = m < first ? 0 : (m - first + 1) * total / (NM - first);
+                static_range<lo, hi>([&](auto o_c) {
+                    constexpr int o = decltype(o_c)::value;
+                    constexpr int kind = step_op_kind(o, NR, nw), idx = step_op_index(o, NR, nw);
+                    if constexpr (kind == 0) {
+                        read_frag(cur ^ 1, rstage, rks, idx);
+                    } else {
+                        constexpr bool is_a = idx < a1 - a0;
+                        constexpr int pass = is_a ? a0 + idx : b0 + idx - (a1 - a0);
+                        if constexpr (kind == 1) {
+                            if constexpr (is_a) opa.store(smem, pass, NXT, SET);
+                            else opb.store(smem, pass, NXT, SET);
+                        } else {
+                            if constexpr (is_a) opa.load(pass, SET);
+                            else opb.load(pass, SET);
+                        }
+                    }
+                });
+                __builtin_amdgcn_sched_barrier(0);
+            });
+            // keep this step's fragments live to the end of the step, so the
+            // next step's reads land in other registers
+#pragma unroll
+            for (int j = 0; j < FN; ++j) asm volatile("" ::"v"(bf[cur][j]));
+#pragma unroll
+            for (int i = 0; i < FM; ++i) asm volatile("" ::"v"(af[cur][i]));
+        });
+    };
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
+    // K-tiles go in pairs (stage 0, stage 1) with no branch between them.
+    // When the count is odd the last pair's second K-tile lies past K: its
+    // stage holds zeros, so its MFMAs add +0 to accumulators that are never
+    // -0 (they start at +0), which leaves every bit unchanged.
+    for (int kt = 0; kt < kt_count; kt += 2) {
+        k_iter(S0{}, kt);
+        k_iter(S1{}, kt + 1);
+    }
+
+    store_tile<C, NN, OpA::kLdsBytes + OpB::kLdsBytes>(acc, smem, p, m0, n0, wm, wn, wave, lane);
+}
+
+
 
 // Fill the output with +0 (K == 0: the zero accumulator is what gets stored).
 template <class T>

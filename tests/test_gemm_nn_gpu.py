@@ -26,7 +26,7 @@ pytestmark = pytest.mark.gpu
 
 GUARD = 32  # fp32 elements of sentinel on each side of D
 SENTINEL = np.float32(-12345.5)
-NN_TILES = [t for t in sorted(g.TILES) if t != g.TILE_128x128_M16]
+NN_TILES = [t for t in sorted(g.TILES) if t not in g.M16_TILES]
 
 
 @pytest.fixture(scope="module", autouse=True)
