@@ -1,6 +1,8 @@
 """Offline sweep of block tile and rasterization options on one GPU.
 
     python -m dense_fp16_gemm_f16_amd.tune [--shapes M,N,K ...] [--rounds 3]
+    python -m dense_fp16_gemm_f16_amd.tune --data      # operand values vs time
+    python -m dense_fp16_gemm_f16_amd.tune --ceiling   # MFMA rate, no HBM traffic
 
 For every shape (default: the five benchmark workloads) it times each block
 tile (and, for the default tile, a few swizzle widths) with HIP events,
@@ -29,11 +31,16 @@ def main(argv=None) -> int:
     ap.add_argument("--data", action="store_true",
                     help="instead: time the automatic configuration on one shape (default 8192^3) "
                          "with different operand values (zeros, ones, {-8..8}/8, U[0,1], U[-1,1], N(0,1))")
+    ap.add_argument("--ceiling", action="store_true",
+                    help="instead: the sustained v_mfma_f32_32x32x16_f16 rate of the device with no "
+                         "global memory traffic (libmfma_ceiling.so), on random and on zero operands")
     a = ap.parse_args(argv)
     import torch
 
     if a.data:
         return data_sweep(a, torch)
+    if a.ceiling:
+        return ceiling(a, torch)
 
     shapes = ([tuple(int(x) for x in s.split(",")) for s in a.shapes] if a.shapes else
               [(w.m, w.n, w.k) for w in inputs.WORKLOADS.values()])
@@ -114,6 +121,51 @@ def data_sweep(a, torch) -> int:
         us = statistics.median(t) * 1e3
         print(json.dumps({"shape": [m, n, k], "operands": name, "us": round(us, 1),
                           "tflops": round(2.0 * m * n * k / (us * 1e-6) / 1e12, 1)}), flush=True)
+    return 0
+
+
+def ceiling(a, torch) -> int:
+    """Sustained MFMA rate on a 128x128 wave tile, fragments from LDS (variant
+    0) or registers (variant 1), operands uniform[-1,1] fp16 or zeros."""
+    import ctypes
+    import os
+
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmfma_ceiling.so")
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built: run dense_fp16_gemm_f16_amd.build")
+    L = ctypes.CDLL(path)
+    L.mfma_ceiling_launch.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p,
+                                      ctypes.c_void_p, ctypes.c_void_p]
+    L.mfma_ceiling_flops.argtypes = [ctypes.c_int64, ctypes.c_int32]
+    L.mfma_ceiling_flops.restype = ctypes.c_double
+    wgs = torch.cuda.get_device_properties(0).multi_processor_count
+    iters = 60000  # ~40 ms per launch at 1.5 GHz: long enough for the clock to settle
+    out = torch.empty(wgs * 256, device="cuda", dtype=torch.float32)
+    gen = torch.Generator(device="cuda").manual_seed(7)
+    tables = {"uniform[-1,1]": (torch.rand(4096 * 8, device="cuda", generator=gen) * 2 - 1).half(),
+              "zeros": torch.zeros(4096 * 8, device="cuda", dtype=torch.float16)}
+    stream = torch.cuda.current_stream()
+    names = {0: "fragments from LDS", 1: "fragments in registers"}
+    for operands, t in tables.items():
+        for variant in (0, 1):
+            def run(n):
+                rc = L.mfma_ceiling_launch(variant, n, wgs, t.data_ptr(), out.data_ptr(), stream.cuda_stream)
+                if rc != 0:
+                    raise RuntimeError(f"mfma_ceiling_launch returned {rc}")
+            run(iters // 20)
+            ms = []
+            for _ in range(max(a.rounds, 3)):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                run(iters)
+                e1.record(stream)
+                torch.cuda.synchronize()
+                ms.append(e0.elapsed_time(e1))
+            med = statistics.median(ms)
+            tf = L.mfma_ceiling_flops(iters, wgs) / (med * 1e-3) / 1e12
+            print(json.dumps({"probe": "v_mfma_f32_32x32x16_f16, 128x128 wave tile", "variant": names[variant],
+                              "operands": operands, "workgroups": wgs, "ms": round(med, 2),
+                              "tflops": round(tf, 1)}), flush=True)
     return 0
 
 

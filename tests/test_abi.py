@@ -30,6 +30,27 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(L, name), name
 
 
+def test_ceiling_probe_exports_its_header():
+    """libmfma_ceiling.so (the MFMA-rate probe) exports what its header declares."""
+    hdr = open(os.path.join(ROOT, "include", "mfma_ceiling.h")).read()
+    hdr = re.sub(r"/\*.*?\*/", "", hdr, flags=re.S)
+    declared = sorted(set(re.findall(r"\b(mfma_ceiling_\w+)\s*\(", hdr)))
+    assert declared == ["mfma_ceiling_flops", "mfma_ceiling_launch"]
+    L = ctypes.CDLL(os.path.join(ROOT, "dense_fp16_gemm_f16_amd", "libmfma_ceiling.so"))
+    for name in declared:
+        assert hasattr(L, name), name
+    L.mfma_ceiling_launch.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p,
+                                      ctypes.c_void_p, ctypes.c_void_p]
+    L.mfma_ceiling_flops.argtypes = [ctypes.c_int64, ctypes.c_int32]
+    L.mfma_ceiling_flops.restype = ctypes.c_double
+    # argument checks return before any HIP call
+    assert L.mfma_ceiling_launch(2, 1, 1, 16, 16, None) == -1
+    assert L.mfma_ceiling_launch(0, 0, 1, 16, 16, None) == -1
+    assert L.mfma_ceiling_launch(0, 1, 1, None, 16, None) == -2
+    assert L.mfma_ceiling_launch(0, 1, 1, 8, 16, None) == -3
+    assert L.mfma_ceiling_flops(10, 256) == 10 * 2 * 16 * 32768 * 4 * 256
+
+
 def test_status_strings():
     for code in (g.OK, g.EINVAL, g.ENULL, g.EALIGN, g.EDEVICE, g.EHIP, g.EOVERLAP):
         s = g.status_string(code)
