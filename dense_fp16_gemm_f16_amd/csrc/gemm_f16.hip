@@ -168,9 +168,14 @@ __device__ __forceinline__ void lds_barrier() {
 // GEMM_PLANE_PAD bytes.  Each pass of the workgroup covers RPP rows of the
 // K-tile (ROWS x 64 fp16 = ROWS x 8 chunks of 16 bytes); thread t owns
 // chunk t % 8 of rows t / 8 + RPP * i, so every 8 consecutive lanes read one
-// 128-byte row segment.
-template <class C, int ROWS, int WROWS, bool VEC, bool KFULL, int SETS>
+// 128-byte row segment.  G: fp16 elements per global load, the largest the
+// alignment of the rows allows: 8 (one 16-byte load per chunk), 4 (two
+// 8-byte loads), 2 (four 4-byte loads) or 1 (eight 2-byte loads).
+template <class C, int ROWS, int WROWS, int G, bool KFULL, int SETS>
 struct KMajorOperand {
+    static constexpr bool VEC = G == 8;
+    static constexpr int kUnits = 8 / G;  // loads per 16-byte chunk
+    static_assert(G == 8 || G == 4 || G == 2 || G == 1, "load granularity");
     static constexpr int RPP = C::kRowsPerPass;
     static constexpr int kPasses = ROWS / RPP;
     static constexpr int kPlane = ROWS * 32 + GEMM_PLANE_PAD;
@@ -184,12 +189,13 @@ struct KMajorOperand {
                   "LDS immediates must fit the 16-bit offset field");
 
     int4v regs[SETS][kPasses];
-    uint32_t voff[kPasses];  // VEC: byte offset of this lane's chunk from the K-tile start
+    uint32_t voff[kPasses];  // G > 1: byte offset of this lane's chunk from the K-tile start
     int chunk, row0, k_elems, k_tiles;
     const _Float16 *tile;
     uint32_t bytes;
     __amdgpu_buffer_rsrc_t rsrc0, rsrc_t, rsrc_none;
-    uint32_t mask;
+    uint32_t mask;               // G == 8: the chunk past K
+    uint32_t umask[kUnits];      // 1 < G < 8: each load unit of the chunk past K
     uint32_t soff;  // KFULL: byte offset of the K-tile inside each row
     int k0;
     int w_lane, r_lane;
@@ -237,6 +243,9 @@ struct KMajorOperand {
             rsrc_t = make_rsrc(tile + (live ? t * C::BK : 0), (live && bytes > skip) ? bytes - skip : 0u);
             soff = 0;
             mask = (k0 + chunk * 8 >= k_elems) ? kOutOfRange : 0u;
+            // K % G == 0: a unit of G elements is wholly inside or wholly past K
+#pragma unroll
+            for (int u = 0; u < kUnits; ++u) umask[u] = (k0 + chunk * 8 + u * G >= k_elems) ? kOutOfRange : 0u;
         }
     }
 
@@ -246,6 +255,17 @@ struct KMajorOperand {
                 regs[set][i] = __builtin_amdgcn_raw_buffer_load_b128(rsrc_t, voff[i], soff, 0);
             else
                 regs[set][i] = __builtin_amdgcn_raw_buffer_load_b128(rsrc_t, voff[i] | mask, 0, 0);
+        } else if constexpr (G == 4) {
+            typedef int int2v __attribute__((ext_vector_type(2)));
+            const int2v lo = __builtin_amdgcn_raw_buffer_load_b64(rsrc_t, voff[i] | umask[0], 0, 0);
+            const int2v hi = __builtin_amdgcn_raw_buffer_load_b64(rsrc_t, (voff[i] + 8u) | umask[1], 0, 0);
+            regs[set][i] = int4v{lo[0], lo[1], hi[0], hi[1]};
+        } else if constexpr (G == 2) {
+            int4v r;
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                r[u] = __builtin_amdgcn_raw_buffer_load_b32(rsrc_t, (voff[i] + 4u * u) | umask[u], 0, 0);
+            regs[set][i] = r;
         } else {
             // every element bounds-checked against K; rows past the tile's
             // valid rows are past num_records
@@ -437,7 +457,9 @@ __device__ __forceinline__ void store_tile(const typename Mfma<C::MB>::Acc (&acc
             const int4v v = *reinterpret_cast<const int4v *>(stg + r * RB + ((c ^ (r % CPR)) << 4));
             const int m = m0 + wm * TM + pass * SR + r;
             const int n = n0 + wn * TN + c * (16 / ES);
-            if (m < p.m) {
+            // chunks wholly past N store nothing; only a chunk that straddles
+            // N (or an unaligned C) takes the per-element path
+            if (m < p.m && n < p.n) {
                 Out *crow = static_cast<Out *>(p.c) + (int64_t)m * p.n;
                 if (vec16 && n + 16 / ES - 1 < p.n) {
                     *reinterpret_cast<int4v *>(crow + n) = v;
@@ -498,8 +520,10 @@ constexpr int step_op_index(int o, int nr, int nw) {
 //
 // NN == false: C fp16 [M,N] = A [M,K] * B[N,K]^T (the tutorial's contract).
 // NN == true:  D fp32 [M,N] = A [M,K] * B[K,N]   (the day-78 listing's).
-// KFULL: VEC and K a multiple of the K-tile (one descriptor per operand).
-template <class C, bool VEC, bool NN, bool KFULL>
+// G: elements per global load of the K-major operands (8 = the 16-byte
+// path); KFULL: G == 8 and K a multiple of the K-tile (one descriptor per
+// operand).
+template <class C, int G, bool NN, bool KFULL>
 __global__ __launch_bounds__(C::kThreads)
 __attribute__((amdgpu_waves_per_eu(C::kMinWavesPerEU, C::kMinWavesPerEU)))
 void gemm_f16_kernel(const Params p) {
@@ -507,9 +531,11 @@ void gemm_f16_kernel(const Params p) {
     constexpr int TM = C::TM, TN = C::TN, FM = C::FM, FN = C::FN, MB = C::MB;
     // the scalar loader's per-element loads keep too many registers in
     // flight for a second staging set
+    constexpr bool VEC = G == 8;
+    static_assert(!NN || G == 8 || G == 1, "D = A B: 16-byte or per-element loads");
     constexpr int SETS = VEC ? C::kSets : 1;
-    using OpA = KMajorOperand<C, BM, TM, VEC, KFULL, SETS>;
-    using OpB = std::conditional_t<NN, NMajorB<C, VEC, SETS>, KMajorOperand<C, BN, TN, VEC, KFULL, SETS>>;
+    using OpA = KMajorOperand<C, BM, TM, G, KFULL, SETS>;
+    using OpB = std::conditional_t<NN, NMajorB<C, VEC, SETS>, KMajorOperand<C, BN, TN, G, KFULL, SETS>>;
     constexpr int PA = OpA::kPasses, PB = OpB::kPasses;
     constexpr int kLdsB = OpA::kLdsBytes;
     static_assert(OpA::kLdsBytes + OpB::kLdsBytes <= 160 * 1024, "LDS budget");
@@ -779,25 +805,33 @@ static int check_device() {
 }
 
 template <class C, bool NN>
-static void launch(const Params &p, bool vec, hipStream_t stream) {
+static void launch(const Params &p, int g, hipStream_t stream) {
     const dim3 grid((unsigned)((int64_t)p.num_m * p.num_n));
-    if (vec && p.k % C::BK == 0)
-        hipLaunchKernelGGL((gemm_f16_kernel<C, true, NN, true>), grid, dim3(C::kThreads), 0, stream, p);
-    else if (vec)
-        hipLaunchKernelGGL((gemm_f16_kernel<C, true, NN, false>), grid, dim3(C::kThreads), 0, stream, p);
-    else
-        hipLaunchKernelGGL((gemm_f16_kernel<C, false, NN, false>), grid, dim3(C::kThreads), 0, stream, p);
+    if (g == 8 && p.k % C::BK == 0)
+        hipLaunchKernelGGL((gemm_f16_kernel<C, 8, NN, true>), grid, dim3(C::kThreads), 0, stream, p);
+    else if (g == 8)
+        hipLaunchKernelGGL((gemm_f16_kernel<C, 8, NN, false>), grid, dim3(C::kThreads), 0, stream, p);
+    else if constexpr (!NN) {
+        if (g == 4)
+            hipLaunchKernelGGL((gemm_f16_kernel<C, 4, NN, false>), grid, dim3(C::kThreads), 0, stream, p);
+        else if (g == 2)
+            hipLaunchKernelGGL((gemm_f16_kernel<C, 2, NN, false>), grid, dim3(C::kThreads), 0, stream, p);
+        else
+            hipLaunchKernelGGL((gemm_f16_kernel<C, 1, NN, false>), grid, dim3(C::kThreads), 0, stream, p);
+    } else {
+        hipLaunchKernelGGL((gemm_f16_kernel<C, 1, NN, false>), grid, dim3(C::kThreads), 0, stream, p);
+    }
 }
 
 template <bool NN>
-static void launch_tile(int tile, const Params &p, bool vec, hipStream_t s) {
+static void launch_tile(int tile, const Params &p, int g, hipStream_t s) {
     switch (tile) {
-        case GEMM_F16_TILE_256x256: launch<Cfg256, NN>(p, vec, s); break;
-        case GEMM_F16_TILE_256x256_W8: launch<Cfg256w8, NN>(p, vec, s); break;
-        case GEMM_F16_TILE_256x128: launch<Cfg256x128, NN>(p, vec, s); break;
-        case GEMM_F16_TILE_128x256: launch<Cfg128x256, NN>(p, vec, s); break;
-        case GEMM_F16_TILE_128x128: launch<Cfg128, NN>(p, vec, s); break;
-        default: launch<Cfg64, NN>(p, vec, s); break;
+        case GEMM_F16_TILE_256x256: launch<Cfg256, NN>(p, g, s); break;
+        case GEMM_F16_TILE_256x256_W8: launch<Cfg256w8, NN>(p, g, s); break;
+        case GEMM_F16_TILE_256x128: launch<Cfg256x128, NN>(p, g, s); break;
+        case GEMM_F16_TILE_128x256: launch<Cfg128x256, NN>(p, g, s); break;
+        case GEMM_F16_TILE_128x128: launch<Cfg128, NN>(p, g, s); break;
+        default: launch<Cfg64, NN>(p, g, s); break;
     }
 }
 
@@ -848,17 +882,25 @@ static int gemm_impl(bool nn, int64_t m, int64_t n, int64_t k, const void *a, co
     p.k_tiles = (int32_t)cdiv(k, 64);
     p.swizzle = o.swizzle ? o.swizzle : 4;
     p.xcd = o.xcd < 0 ? 1 : o.xcd;
-    // 16-byte loads need 16-byte aligned rows of A, and of B in its layout
-    const bool vec = (k % 8) == 0 && (!nn || (n % 8) == 0) && ((uintptr_t)a % 16) == 0 &&
-                     ((uintptr_t)b % 16) == 0;
+    // Elements per global load: 16-byte loads need 16-byte aligned rows of
+    // A, and of B in its layout; for C = A B^T, 8- and 4-byte loads serve
+    // rows aligned to 8 or 4 bytes; otherwise one element per load.
+    const uintptr_t ab = (uintptr_t)a | (uintptr_t)b;
+    int g = 1;
+    if ((k % 8) == 0 && (!nn || (n % 8) == 0) && (ab % 16) == 0)
+        g = 8;
+    else if (!nn && (k % 4) == 0 && (ab % 8) == 0)
+        g = 4;
+    else if (!nn && (k % 2) == 0 && (ab % 4) == 0)
+        g = 2;
     if ((int64_t)p.num_m * p.num_n >= (int64_t(1) << 31)) return GEMM_F16_EINVAL;
 
     if (nn) {
-        launch_tile<true>(tile, p, vec, s);
+        launch_tile<true>(tile, p, g, s);
     } else if (tile == GEMM_F16_TILE_128x128_M16) {
-        launch<Cfg128m16, false>(p, vec, s);
+        launch<Cfg128m16, false>(p, g, s);
     } else {
-        launch_tile<false>(tile, p, vec, s);
+        launch_tile<false>(tile, p, g, s);
     }
     return hipGetLastError() == hipSuccess ? GEMM_F16_OK : GEMM_F16_EHIP;
 }

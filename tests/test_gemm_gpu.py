@@ -169,6 +169,30 @@ def test_ragged_shapes(m, n, k, tile):
     assert_ulp(run_gemm(a, b, tile=tile), oracle.gemm_f16_nt(a, b), k, f"{m}x{n}x{k}")
 
 
+# K and operand offsets (in elements) chosen so each global-load width runs:
+# 8-byte loads (K % 4 == 0 and rows 8-byte aligned), 4-byte loads (K % 2 == 0
+# and rows 4-byte aligned) and one element per load (odd K).
+GRANULARITY = [
+    (100, 0, 0), (132, 0, 0), (2500, 0, 0), (4, 0, 0),  # K % 8 == 4: 8-byte loads
+    (98, 0, 0), (130, 0, 0), (6, 0, 0), (1026, 0, 0),   # K % 4 == 2: 4-byte loads
+    (96, 4, 0), (96, 0, 4),                             # K % 8 == 0, an operand 8-byte aligned
+    (96, 2, 0), (64, 0, 6),                             # ... an operand 4-byte aligned
+    (99, 0, 0),                                         # odd K: one element per load
+]
+
+
+@pytest.mark.parametrize("k,a_off,b_off", GRANULARITY)
+@pytest.mark.parametrize("tile", TILES)
+def test_load_widths_bit_exact(k, a_off, b_off, tile):
+    _announce("load widths", k, a_off, b_off, tile)
+    rng = np.random.default_rng(k * 31 + a_off * 7 + b_off)
+    m, n = 150, 140
+    a = (rng.integers(-8, 9, size=(m, k)) / 8).astype(np.float16)
+    b = (rng.integers(-8, 9, size=(n, k)) / 8).astype(np.float16)
+    got = run_gemm(a, b, a_offset=a_off, b_offset=b_off, tile=tile)
+    assert_bits_equal(got, oracle.gemm_f16_nt(a, b), f"K={k} offsets {a_off},{b_off} tile {tile}")
+
+
 @pytest.mark.parametrize("a_off,b_off", [(1, 0), (0, 3), (5, 7)])
 def test_unaligned_operands_take_the_scalar_loader(a_off, b_off):
     _announce("unaligned", a_off, b_off)
