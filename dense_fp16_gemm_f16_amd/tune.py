@@ -125,8 +125,10 @@ def data_sweep(a, torch) -> int:
 
 
 def ceiling(a, torch) -> int:
-    """Sustained MFMA rate on a 128x128 wave tile, fragments from LDS (variant
-    0) or registers (variant 1), operands uniform[-1,1] fp16 or zeros."""
+    """Sustained MFMA rate on a 128x128 wave tile: v_mfma_f32_32x32x16_f16
+    with fragments from LDS (variant 0) or registers (variant 1), and
+    v_mfma_f32_16x16x32_f16 with tied accumulators, the same two ways
+    (variants 2, 3); operands uniform[-1,1] fp16 or zeros."""
     import ctypes
     import os
 
@@ -145,9 +147,12 @@ def ceiling(a, torch) -> int:
     tables = {"uniform[-1,1]": (torch.rand(4096 * 8, device="cuda", generator=gen) * 2 - 1).half(),
               "zeros": torch.zeros(4096 * 8, device="cuda", dtype=torch.float16)}
     stream = torch.cuda.current_stream()
-    names = {0: "fragments from LDS", 1: "fragments in registers"}
+    names = {0: "fragments from LDS", 1: "fragments in registers", 2: "fragments from LDS",
+             3: "fragments in registers"}
+    probes = {0: "v_mfma_f32_32x32x16_f16", 1: "v_mfma_f32_32x32x16_f16",
+              2: "v_mfma_f32_16x16x32_f16 (tied)", 3: "v_mfma_f32_16x16x32_f16 (tied)"}
     for operands, t in tables.items():
-        for variant in (0, 1):
+        for variant in (0, 1, 2, 3):
             def run(n):
                 rc = L.mfma_ceiling_launch(variant, n, wgs, t.data_ptr(), out.data_ptr(), stream.cuda_stream)
                 if rc != 0:
@@ -163,7 +168,7 @@ def ceiling(a, torch) -> int:
                 ms.append(e0.elapsed_time(e1))
             med = statistics.median(ms)
             tf = L.mfma_ceiling_flops(iters, wgs) / (med * 1e-3) / 1e12
-            print(json.dumps({"probe": "v_mfma_f32_32x32x16_f16, 128x128 wave tile", "variant": names[variant],
+            print(json.dumps({"probe": probes[variant] + ", 128x128 wave tile", "variant": names[variant],
                               "operands": operands, "workgroups": wgs, "ms": round(med, 2),
                               "tflops": round(tf, 1)}), flush=True)
     return 0

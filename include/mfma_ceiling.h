@@ -1,7 +1,8 @@
 /*
  * mfma_ceiling.h - C ABI of libmfma_ceiling.so, a measurement probe (not part
- * of the GEMM): the sustained v_mfma_f32_32x32x16_f16 rate of the device with
- * no global memory traffic in the loop, on operand values the caller chooses.
+ * of the GEMM): the sustained v_mfma_f32_32x32x16_f16 and
+ * v_mfma_f32_16x16x32_f16 rates of the device with no global memory traffic
+ * in the loop, on operand values the caller chooses.
  * It is the practical ceiling against which the GEMM's fraction of the
  * published dense fp16 peak is read (the MFMA clock falls with the switching
  * activity of the operands).
@@ -21,9 +22,11 @@ extern "C" {
 /*
  * Enqueue one launch on `stream` (hipStream_t as void*; NULL = null stream):
  * `workgroups` workgroups of 4 waves (use one per CU), each wave running
- * `iters` iterations of two 16-wide k steps of 16 MFMAs on a 128x128 fp32
- * tile.  variant 0: the operand fragments are re-read from LDS every k step;
- * variant 1: they stay in registers.
+ * `iters` iterations on a 128x128 fp32 tile.  Variants 0 and 1: an iteration
+ * is two 16-wide k steps of 16 v_mfma_f32_32x32x16_f16; variants 2 and 3:
+ * one 32-wide k step of 64 v_mfma_f32_16x16x32_f16 with the accumulators
+ * tied in AGPRs (the same flops).  Variants 0 and 2 re-read the operand
+ * fragments from LDS every k step; 1 and 3 keep them in registers.
  *   table  device pointer, 16-byte aligned, MFMA_CEILING_TABLE_ENTRIES x 16
  *          bytes of fp16 operand values (copied to LDS, read by every wave)
  *   out    device pointer, workgroups * 256 floats (sums that keep the

@@ -44,7 +44,8 @@ def test_ceiling_probe_exports_its_header():
     L.mfma_ceiling_flops.argtypes = [ctypes.c_int64, ctypes.c_int32]
     L.mfma_ceiling_flops.restype = ctypes.c_double
     # argument checks return before any HIP call
-    assert L.mfma_ceiling_launch(2, 1, 1, 16, 16, None) == -1
+    assert L.mfma_ceiling_launch(4, 1, 1, 16, 16, None) == -1
+    assert L.mfma_ceiling_launch(-1, 1, 1, 16, 16, None) == -1
     assert L.mfma_ceiling_launch(0, 0, 1, 16, 16, None) == -1
     assert L.mfma_ceiling_launch(0, 1, 1, None, 16, None) == -2
     assert L.mfma_ceiling_launch(0, 1, 1, 8, 16, None) == -3

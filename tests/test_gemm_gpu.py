@@ -193,6 +193,22 @@ def test_load_widths_bit_exact(k, a_off, b_off, tile):
     assert_bits_equal(got, oracle.gemm_f16_nt(a, b), f"K={k} offsets {a_off},{b_off} tile {tile}")
 
 
+# K a multiple of the 64-wide K-tile with 16-byte aligned rows: the loads go
+# straight into LDS.  1, 2, 3, 5 and 15 K-tiles (odd counts end on the first
+# stage), rows and columns past M and N inside the last block tile.
+DIRECT = [(1, 1, 64), (257, 129, 64), (64, 64, 128), (300, 270, 192), (33, 300, 320), (130, 515, 960)]
+
+
+@pytest.mark.parametrize("m,n,k", DIRECT)
+@pytest.mark.parametrize("tile", TILES)
+def test_direct_to_lds_path_bit_exact(m, n, k, tile):
+    _announce("direct", m, n, k, tile)
+    rng = np.random.default_rng(m + 3 * n + 5 * k + tile)
+    a = (rng.integers(-8, 9, size=(m, k)) / 8).astype(np.float16)
+    b = (rng.integers(-8, 9, size=(n, k)) / 8).astype(np.float16)
+    assert_bits_equal(run_gemm(a, b, tile=tile), oracle.gemm_f16_nt(a, b), f"{m}x{n}x{k}")
+
+
 @pytest.mark.parametrize("a_off,b_off", [(1, 0), (0, 3), (5, 7)])
 def test_unaligned_operands_take_the_scalar_loader(a_off, b_off):
     _announce("unaligned", a_off, b_off)
