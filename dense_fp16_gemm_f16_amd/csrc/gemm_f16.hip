@@ -118,6 +118,21 @@ constexpr uint32_t kOutOfRange = 0x80000000u;  // buffer offset past any num_rec
 #ifndef GEMM_DIRECT_BAR_MFMA_M16
 #define GEMM_DIRECT_BAR_MFMA_M16 4
 #endif
+// 1: 16x16x32 direct-to-LDS tiles read fragments a K-tile ahead with two
+// barriers per K-tile (gemm_f16_direct_ahead_kernel)
+#ifndef GEMM_AHEAD
+#define GEMM_AHEAD 1
+#endif
+#ifndef GEMM_AHEAD_REL_MFMA
+#define GEMM_AHEAD_REL_MFMA 4
+#endif
+#ifndef GEMM_AHEAD_ACQ_MFMA
+#define GEMM_AHEAD_ACQ_MFMA 4
+#endif
+// sixteenths of a K-tile's loads issued in step 0 (the rest in step 1)
+#ifndef GEMM_AHEAD_STEP0_LOADS
+#define GEMM_AHEAD_STEP0_LOADS 10
+#endif
 // staging register sets (1 or 2; a second set prefetches one more K-tile)
 #ifndef GEMM_STAGE_SETS
 #define GEMM_STAGE_SETS 1
@@ -1002,6 +1017,188 @@ void gemm_f16_direct_kernel(const Params p) {
     store_tile<C, false, kLds>(acc, smem, p, m0, n0, wm, wn, wave, lane);
 }
 
+// Wait until this wave's LDS reads are done (its global loads may still be
+// in flight), then the workgroup barrier.
+__device__ __forceinline__ void lgkm_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_s_waitcnt(15 | (7 << 4) | (0 << 8) | (3 << 14));
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Wait until at most V of this wave's global loads are in flight (its LDS
+// reads may still be pending), then the workgroup barrier.
+template <int V>
+__device__ __forceinline__ void vm_only_barrier() {
+    static_assert(V >= 0 && V < 64, "vmcnt range");
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_s_waitcnt((V & 15) | (7 << 4) | (15 << 8) | ((V >> 4) << 14));
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Direct-to-LDS kernel for 16x16x32 tiles (two 32-wide k steps per K-tile)
+// with the fragment reads a whole K-tile ahead and two barriers per K-tile.
+// Stage S holds K-tile t.  Both of its steps' fragments are read during
+// step 1 of K-tile t-1, so S is free from the start of K-tile t:
+//   step 0: release barrier (every wave's reads of S are done), then the
+//           MFMAs of step 0 with the first loads of K-tile t+2 into S;
+//   step 1: acquire barrier (every wave's loads of K-tile t+1 into S^1 are
+//           done), then the MFMAs of step 1 with the reads of both steps of
+//           K-tile t+1 from S^1 and the rest of K-tile t+2's loads.
+// The loads of a K-tile thus spread over a whole K-tile, a steady stream
+// instead of a burst after one barrier, and the last of them still have a k
+// step to land.  Fragments rotate over three register buffers: step 0 always
+// uses buffer 0, step 1 uses buffer 1 on stage 0 and buffer 2 on stage 1.
+template <class C>
+__global__ __launch_bounds__(C::kThreads)
+__attribute__((amdgpu_waves_per_eu(C::kMinWavesPerEU, C::kMinWavesPerEU)))
+void gemm_f16_direct_ahead_kernel(const Params p) {
+    constexpr int BM = C::BM, BN = C::BN;
+    constexpr int TM = C::TM, TN = C::TN, FM = C::FM, FN = C::FN;
+    static_assert(C::MB == 16 && C::KS == 2, "two 32-wide k steps per K-tile");
+    using OpA = KMajorDirect<C, BM>;
+    using OpB = KMajorDirect<C, BN>;
+    constexpr int kLdsB = OpA::kLdsBytes;
+    constexpr int kLds = OpA::kLdsBytes + OpB::kLdsBytes;
+    constexpr int LA = OpA::kLoads, L = OpA::kLoads + OpB::kLoads;
+    static_assert(kLds <= 160 * 1024, "LDS budget");
+    static_assert(2 * L < 64, "vmcnt range");
+    static_assert(OpA::kStage + (FM - 1) * C::MB * 128 < 65536 && OpB::kStage + (FN - 1) * C::MB * 128 < 65536,
+                  "LDS immediates must fit the 16-bit offset field");
+    __shared__ __attribute__((aligned(1024))) char smem[kLds];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int wm = wave / C::WN;
+    const int wn = wave % C::WN;
+
+    const TileCoord tc = tile_coord(blockIdx.x, p.num_m, p.num_n, p.swizzle, p.xcd != 0);
+    const int m0 = (int)tc.m_block * BM;
+    const int n0 = (int)tc.n_block * BN;
+    const int kt_count = p.k_tiles;
+    if (kt_count == 0) return;  // never launched with K == 0
+
+    OpA opa;
+    OpB opb;
+    opa.init(p.a + (int64_t)m0 * p.k, min(BM, p.m - m0), p.k, kt_count, wave, lane, wm * TM, 0);
+    opb.init(p.b + (int64_t)n0 * p.k, min(BN, p.n - n0), p.k, kt_count, wave, lane, wn * TN, kLdsB);
+
+    floatx4 acc[FN][FM];
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int i = 0; i < FM; ++i) acc[j][i] = floatx4{};
+    acc_fence(acc);
+
+    half8 af[3][FM];
+    half8 bf[3][FN];
+    constexpr int NR = FM + FN;  // fragment reads per k step
+    // read r of the 2 NR reads of K-tile t+1: step r / NR, in the order the
+    // MFMAs consume them (B0, A0..A(FM-1), B1..)
+    auto read_frag = [&](int buf, int stage, int ks, int r) {
+        if (r == 0)
+            bf[buf][0] = opb.read(smem, stage, ks, 0);
+        else if (r <= FM)
+            af[buf][r - 1] = opa.read(smem, stage, ks, r - 1);
+        else
+            bf[buf][r - FM] = opb.read(smem, stage, ks, r - FM);
+    };
+    auto load = [&](auto s_c, int t, int i) {
+        constexpr int S = decltype(s_c)::value;
+        if (i < LA)
+            opa.template load<S>(smem, t, i);
+        else
+            opb.template load<S>(smem, t, i - LA);
+    };
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
+    constexpr int NM = FM * FN;
+    constexpr int kRelAt = GEMM_AHEAD_REL_MFMA < NM ? GEMM_AHEAD_REL_MFMA : NM - 1;
+    constexpr int kAcqAt = GEMM_AHEAD_ACQ_MFMA < NM ? GEMM_AHEAD_ACQ_MFMA : NM - 1;
+    constexpr int L0 = L * GEMM_AHEAD_STEP0_LOADS / 16;  // loads of K-tile t+2 in step 0
+
+    // Prologue: K-tiles 0 and 1 into stages 0 and 1; both steps' fragments
+    // of K-tile 0 into buffers 0 and 1.
+#pragma unroll
+    for (int i = 0; i < L; ++i) load(S0{}, 0, i);
+#pragma unroll
+    for (int i = 0; i < L; ++i) load(S1{}, 1, i);
+    vm_barrier<L>();
+#pragma unroll
+    for (int r = 0; r < NR; ++r) read_frag(0, 0, 0, r);
+#pragma unroll
+    for (int r = 0; r < NR; ++r) read_frag(1, 0, 1, r);
+
+    auto k_iter = [&](auto s_c, int t) {
+        constexpr int S = decltype(s_c)::value;
+        constexpr int SN = S ^ 1;
+        using SNc = std::integral_constant<int, SN>;
+        constexpr int B1 = S == 0 ? 1 : 2;   // this K-tile's step-1 buffer
+        constexpr int NB1 = S == 0 ? 2 : 1;  // the next K-tile's
+        // step 0
+        static_range<0, NM>([&](auto m_c) {
+            constexpr int m = decltype(m_c)::value;
+            constexpr int j = m / FM, i = (j & 1) ? FM - 1 - m % FM : m % FM;
+            mfma16_tied(bf[0][j], af[0][i], acc[j][i]);
+            if constexpr (m == kRelAt) lgkm_barrier();
+            if constexpr (m >= kRelAt) {
+                constexpr int q = m - kRelAt, slots = NM - kRelAt;
+                static_range<q * L0 / slots, (q + 1) * L0 / slots>(
+                    [&](auto o_c) { load(s_c, t + 2, decltype(o_c)::value); });
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        });
+#pragma unroll
+        for (int j = 0; j < FN; ++j) asm volatile("" ::"v"(bf[0][j]));
+#pragma unroll
+        for (int i = 0; i < FM; ++i) asm volatile("" ::"v"(af[0][i]));
+        // step 1
+        static_range<0, NM>([&](auto m_c) {
+            constexpr int m = decltype(m_c)::value;
+            constexpr int j = m / FM, i = (j & 1) ? FM - 1 - m % FM : m % FM;
+            mfma16_tied(bf[B1][j], af[B1][i], acc[j][i]);
+            if constexpr (m == kAcqAt) vm_only_barrier<L0>();
+            if constexpr (m >= kAcqAt) {
+                constexpr int nl = L - L0, total = 2 * NR + nl, slots = NM - kAcqAt, q = m - kAcqAt;
+                // R R L R R L ...: the reads first while both remain
+                static_range<q * total / slots, (q + 1) * total / slots>([&](auto o_c) {
+                    constexpr int o = decltype(o_c)::value;
+                    constexpr int groups = (2 * NR) / 2 < nl ? (2 * NR) / 2 : nl;  // (R, R, L) groups
+                    constexpr bool in_groups = o < 3 * groups;
+                    constexpr bool is_read = in_groups ? (o % 3 != 2) : (2 * NR > 2 * groups);
+                    constexpr int idx = in_groups ? (is_read ? (o / 3) * 2 + (o % 3) : o / 3)
+                                                  : (is_read ? 2 * groups + (o - 3 * groups) : groups + (o - 3 * groups));
+                    if constexpr (is_read) {
+                        constexpr int ks = idx / NR, r = idx % NR;
+                        read_frag(ks == 0 ? 0 : NB1, SN, ks, r);
+                    } else {
+                        load(s_c, t + 2, L0 + idx);
+                    }
+                });
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        });
+#pragma unroll
+        for (int j = 0; j < FN; ++j) asm volatile("" ::"v"(bf[B1][j]));
+#pragma unroll
+        for (int i = 0; i < FM; ++i) asm volatile("" ::"v"(af[B1][i]));
+    };
+    // K-tiles in pairs (stage 0, stage 1); an odd count ends with one more
+    // K-tile on stage 0.  Loads past K fill stages that are never summed.
+    int kt = 0;
+    for (; kt + 1 < kt_count; kt += 2) {
+        k_iter(S0{}, kt);
+        k_iter(S1{}, kt + 1);
+    }
+    if (kt < kt_count) k_iter(S0{}, kt);
+
+    vm_barrier<0>();  // no load is still writing LDS when the epilogue stages C there
+    acc_fence(acc);
+    store_tile<C, false, kLds>(acc, smem, p, m0, n0, wm, wn, wave, lane);
+}
+
 
 // Fill the output with +0 (K == 0: the zero accumulator is what gets stored).
 template <class T>
@@ -1116,7 +1313,10 @@ static void launch(const Params &p, int g, hipStream_t stream) {
     const dim3 grid((unsigned)((int64_t)p.num_m * p.num_n));
     if constexpr (!NN && GEMM_DIRECT) {
         if (g == 8 && p.k % CD::BK == 0) {
-            hipLaunchKernelGGL((gemm_f16_direct_kernel<CD>), grid, dim3(CD::kThreads), 0, stream, p);
+            if constexpr (GEMM_AHEAD && CD::MB == 16)
+                hipLaunchKernelGGL((gemm_f16_direct_ahead_kernel<CD>), grid, dim3(CD::kThreads), 0, stream, p);
+            else
+                hipLaunchKernelGGL((gemm_f16_direct_kernel<CD>), grid, dim3(CD::kThreads), 0, stream, p);
             return;
         }
     }
