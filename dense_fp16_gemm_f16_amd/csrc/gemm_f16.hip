@@ -14,8 +14,8 @@
 //               each operand tile, so rows past M / N read as zero; when K
 //               is a multiple of the K-tile one descriptor serves the whole
 //               K walk and the K-tile offset rides in the scalar offset.
-//               For C = A B^T with K a multiple of the K-tile and 16-byte
-//               aligned operands the loads go straight into LDS instead
+//               For C = A B^T with K a multiple of 8 and 16-byte aligned
+//               operands the loads go straight into LDS instead
 //               (gemm_f16_direct_kernel: no staging registers, no LDS
 //               write instructions);
 //  * LDS        a stage holds each operand as four 16-wide k planes of
@@ -92,8 +92,8 @@ constexpr uint32_t kOutOfRange = 0x80000000u;  // buffer offset past any num_rec
 #ifndef GEMM_BAR_MFMA
 #define GEMM_BAR_MFMA 2
 #endif
-// 1: the C = A B^T 16-byte path with K a multiple of the K-tile loads
-// straight into LDS (gemm_f16_direct_kernel)
+// 1: the C = A B^T 16-byte path (K % 8 == 0, 16-byte aligned operands)
+// loads straight into LDS (gemm_f16_direct_kernel, _ahead_kernel)
 #ifndef GEMM_DIRECT
 #define GEMM_DIRECT 1
 #endif
@@ -761,7 +761,7 @@ void gemm_f16_kernel(const Params p) {
 }
 
 
-// ---- direct-to-LDS variant (C = A B^T, K a multiple of the K-tile) --------
+// ---- direct-to-LDS variant (C = A B^T, K % 8 == 0, 16-byte aligned) -------
 //
 // The loads go straight from the buffer unit into LDS (buffer_load_dwordx4
 // with the lds bit: lane l's 16 bytes land at M0 + 16 l), so no staging
@@ -791,7 +791,13 @@ __device__ __forceinline__ void vm_barrier() {
 // Fragments: 32x32x16 lane l takes row l % 32, chunk 2 ks + l / 32 (k step
 // ks of 16); 16x16x32 lane l takes row l % 16, chunk 4 ks + l / 16 (k step
 // ks of 32).
-template <class C, int ROWS>
+// KFULL: K % 64 == 0.  Otherwise (K % 8 == 0) the lanes whose chunk lies
+// past K get an out-of-range offset; an out-of-range lane of a direct load
+// writes zeros into LDS (measured on gfx950), so the partial last K-tile
+// reads as zero-padded.  A lane's chunk index is the same in every load of
+// every K-tile (the swizzle's row bits do not change between a wave's
+// blocks), so the mask is one compare per K-tile.
+template <class C, int ROWS, bool KFULL = true>
 struct KMajorDirect {
     static constexpr int kRow = 128;
     static constexpr int kStage = ROWS * kRow;
@@ -800,16 +806,19 @@ struct KMajorDirect {
     static constexpr int kLoads = kBlocks / C::kWaves;  // per wave and K-tile
     static_assert(C::BK == 64, "a 64-wide K-tile: 8 chunks per row");
     static_assert(kBlocks % C::kWaves == 0, "whole blocks per wave");
+    static_assert(C::kWaves % 2 == 0, "a lane's chunk index is the same in all its loads");
 
     uint32_t voff[kLoads];
     __amdgpu_buffer_rsrc_t rsrc0, rsrc_none;
     int k_tiles;
+    int k_elems, kc;  // !KFULL: K, and k of this lane's chunk inside a K-tile
     int lds_w;     // this wave's first block of stage 0
     int r_lane[C::KS]; // fragment 0 of k step ks in stage 0
 
     __device__ __forceinline__ void init(const _Float16 *base, int rows_valid, int K, int kt_count, int wave,
                                          int lane, int frag_row, int lds) {
         k_tiles = kt_count;
+        k_elems = K;
         rsrc0 = make_rsrc(base, (uint32_t)rows_valid * (uint32_t)K * 2u);
         rsrc_none = make_rsrc(base, 0u);
 #pragma unroll
@@ -817,6 +826,7 @@ struct KMajorDirect {
             const int row = (i * C::kWaves + wave) * 8 + (lane >> 3);
             const int c = (lane & 7) ^ ((row >> 1) & 7);
             voff[i] = (uint32_t)(row * K + c * 8) * 2u;
+            if (i == 0) kc = c * 8;
         }
         lds_w = lds + wave * 1024;
         const int frow = frag_row + lane % C::MB, q = lane / C::MB, sw = (frow >> 1) & 7;
@@ -829,10 +839,12 @@ struct KMajorDirect {
     // load i of K-tile t into stage S; past K an empty range (reads 0)
     template <int S>
     __device__ __forceinline__ void load(char *smem, int t, int i) const {
+        uint32_t vo = voff[i];
+        if constexpr (!KFULL) vo |= (t * C::BK + kc >= k_elems) ? kOutOfRange : 0u;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             t < k_tiles ? rsrc0 : rsrc_none,
             (__attribute__((address_space(3))) void *)(smem + lds_w + S * kStage + i * C::kWaves * 1024), 16,
-            voff[i], (uint32_t)t * 128u, 0, 0);
+            vo, (uint32_t)t * 128u, 0, 0);
     }
 
     __device__ __forceinline__ half8 read(const char *smem, int stage, int ks, int f) const {
@@ -858,14 +870,14 @@ __device__ __forceinline__ void acc_fence(Acc (&acc)[FN][FM]) {
         for (int i = 0; i < FM; ++i) asm volatile("" : "+a"(acc[j][i]));
 }
 
-template <class C>
+template <class C, bool KFULL>
 __global__ __launch_bounds__(C::kThreads)
 __attribute__((amdgpu_waves_per_eu(C::kMinWavesPerEU, C::kMinWavesPerEU)))
 void gemm_f16_direct_kernel(const Params p) {
     constexpr int BM = C::BM, BN = C::BN, KS = C::KS;
     constexpr int TM = C::TM, TN = C::TN, FM = C::FM, FN = C::FN;
-    using OpA = KMajorDirect<C, BM>;
-    using OpB = KMajorDirect<C, BN>;
+    using OpA = KMajorDirect<C, BM, KFULL>;
+    using OpB = KMajorDirect<C, BN, KFULL>;
     constexpr int kLdsB = OpA::kLdsBytes;
     constexpr int kLds = OpA::kLdsBytes + OpB::kLdsBytes;
     constexpr int LA = OpA::kLoads, L = OpA::kLoads + OpB::kLoads;  // loads per wave and K-tile
@@ -1050,15 +1062,15 @@ __device__ __forceinline__ void vm_only_barrier() {
 // instead of a burst after one barrier, and the last of them still have a k
 // step to land.  Fragments rotate over three register buffers: step 0 always
 // uses buffer 0, step 1 uses buffer 1 on stage 0 and buffer 2 on stage 1.
-template <class C>
+template <class C, bool KFULL>
 __global__ __launch_bounds__(C::kThreads)
 __attribute__((amdgpu_waves_per_eu(C::kMinWavesPerEU, C::kMinWavesPerEU)))
 void gemm_f16_direct_ahead_kernel(const Params p) {
     constexpr int BM = C::BM, BN = C::BN;
     constexpr int TM = C::TM, TN = C::TN, FM = C::FM, FN = C::FN;
     static_assert(C::MB == 16 && C::KS == 2, "two 32-wide k steps per K-tile");
-    using OpA = KMajorDirect<C, BM>;
-    using OpB = KMajorDirect<C, BN>;
+    using OpA = KMajorDirect<C, BM, KFULL>;
+    using OpB = KMajorDirect<C, BN, KFULL>;
     constexpr int kLdsB = OpA::kLdsBytes;
     constexpr int kLds = OpA::kLdsBytes + OpB::kLdsBytes;
     constexpr int LA = OpA::kLoads, L = OpA::kLoads + OpB::kLoads;
@@ -1312,11 +1324,16 @@ static void launch(const Params &p, int g, hipStream_t stream) {
     static_assert(CD::BM == C::BM && CD::BN == C::BN, "one block tile");
     const dim3 grid((unsigned)((int64_t)p.num_m * p.num_n));
     if constexpr (!NN && GEMM_DIRECT) {
-        if (g == 8 && p.k % CD::BK == 0) {
-            if constexpr (GEMM_AHEAD && CD::MB == 16)
-                hipLaunchKernelGGL((gemm_f16_direct_ahead_kernel<CD>), grid, dim3(CD::kThreads), 0, stream, p);
-            else
-                hipLaunchKernelGGL((gemm_f16_direct_kernel<CD>), grid, dim3(CD::kThreads), 0, stream, p);
+        if (g == 8) {
+            const dim3 block(CD::kThreads);
+            const bool full = p.k % CD::BK == 0;
+            if constexpr (GEMM_AHEAD && CD::MB == 16) {
+                if (full) hipLaunchKernelGGL((gemm_f16_direct_ahead_kernel<CD, true>), grid, block, 0, stream, p);
+                else hipLaunchKernelGGL((gemm_f16_direct_ahead_kernel<CD, false>), grid, block, 0, stream, p);
+            } else {
+                if (full) hipLaunchKernelGGL((gemm_f16_direct_kernel<CD, true>), grid, block, 0, stream, p);
+                else hipLaunchKernelGGL((gemm_f16_direct_kernel<CD, false>), grid, block, 0, stream, p);
+            }
             return;
         }
     }

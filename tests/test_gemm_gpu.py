@@ -193,10 +193,12 @@ def test_load_widths_bit_exact(k, a_off, b_off, tile):
     assert_bits_equal(got, oracle.gemm_f16_nt(a, b), f"K={k} offsets {a_off},{b_off} tile {tile}")
 
 
-# K a multiple of the 64-wide K-tile with 16-byte aligned rows: the loads go
-# straight into LDS.  1, 2, 3, 5 and 15 K-tiles (odd counts end on the first
-# stage), rows and columns past M and N inside the last block tile.
-DIRECT = [(1, 1, 64), (257, 129, 64), (64, 64, 128), (300, 270, 192), (33, 300, 320), (130, 515, 960)]
+# K % 8 == 0 with 16-byte aligned rows: the loads go straight into LDS.  1,
+# 2, 3, 5 and 15 full K-tiles (odd counts end on the first stage), partial
+# last K-tiles (K % 64 = 8, 40, 56: chunks past K read as zeros), K below one
+# K-tile, rows and columns past M and N inside the last block tile.
+DIRECT = [(1, 1, 64), (257, 129, 64), (64, 64, 128), (300, 270, 192), (33, 300, 320), (130, 515, 960),
+          (1, 1, 8), (70, 90, 40), (300, 270, 200), (257, 129, 1000), (65, 63, 504), (129, 257, 72)]
 
 
 @pytest.mark.parametrize("m,n,k", DIRECT)
