@@ -1224,9 +1224,9 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(T *c, int64_t count) {
 
 using Cfg256 = Cfg<256, 256, 2, 2>;   // 4 waves, 128x128 each
 // the same tile on v_mfma_f32_16x16x32_f16 with tied accumulators: the
-// 256x256 tile's direct-to-LDS path (measured 12-16% faster than 32x32x16
-// there; the register-staged path keeps 32x32x16, whose builtin keeps its
-// accumulators in place)
+// direct-to-LDS path of every 4-wave tile (measured 12-16% faster than
+// 32x32x16 at 256x256 and 7-28% at the smaller tiles; the register-staged
+// path keeps 32x32x16, whose builtin keeps its accumulators in place)
 using Cfg256d = Cfg<256, 256, 2, 2, 16>;
 using Cfg256w8 = Cfg<256, 256, 4, 2>; // 8 waves, 64x128 each
 using Cfg256x128 = Cfg<256, 128, 2, 2>;
@@ -1360,10 +1360,10 @@ static void launch_tile(int tile, const Params &p, int g, hipStream_t s) {
             launch<Cfg256, NN, Cfg256d>(p, g, s);
             break;
         case GEMM_F16_TILE_256x256_W8: launch<Cfg256w8, NN>(p, g, s); break;
-        case GEMM_F16_TILE_256x128: launch<Cfg256x128, NN>(p, g, s); break;
-        case GEMM_F16_TILE_128x256: launch<Cfg128x256, NN>(p, g, s); break;
-        case GEMM_F16_TILE_128x128: launch<Cfg128, NN>(p, g, s); break;
-        default: launch<Cfg64, NN>(p, g, s); break;
+        case GEMM_F16_TILE_256x128: launch<Cfg256x128, NN, Cfg<256, 128, 2, 2, 16>>(p, g, s); break;
+        case GEMM_F16_TILE_128x256: launch<Cfg128x256, NN, Cfg<128, 256, 2, 2, 16>>(p, g, s); break;
+        case GEMM_F16_TILE_128x128: launch<Cfg128, NN, Cfg<128, 128, 2, 2, 16>>(p, g, s); break;
+        default: launch<Cfg64, NN, Cfg<64, 64, 2, 2, 16>>(p, g, s); break;
     }
 }
 
