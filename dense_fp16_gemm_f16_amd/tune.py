@@ -32,7 +32,7 @@ def main(argv=None) -> int:
                     help="instead: time the automatic configuration on one shape (default 8192^3) "
                          "with different operand values (zeros, ones, {-8..8}/8, U[0,1], U[-1,1], N(0,1))")
     ap.add_argument("--ceiling", action="store_true",
-                    help="instead: the sustained v_mfma_f32_32x32x16_f16 rate of the device with no "
+                    help="instead: the sustained v_mfma_f32_32x32x16_f16 and v_mfma_f32_16x16x32_f16 rates of the device with no "
                          "global memory traffic (libmfma_ceiling.so), on random and on zero operands")
     a = ap.parse_args(argv)
     import torch
