@@ -129,6 +129,10 @@ constexpr uint32_t kOutOfRange = 0x80000000u;  // buffer offset past any num_rec
 #ifndef GEMM_AHEAD_ACQ_MFMA
 #define GEMM_AHEAD_ACQ_MFMA 4
 #endif
+// 1: more tiles than CUs -> one workgroup per CU walking several tiles
+#ifndef GEMM_PERSIST
+#define GEMM_PERSIST 1
+#endif
 // sixteenths of a K-tile's loads issued in step 0 (the rest in step 1)
 #ifndef GEMM_AHEAD_STEP0_LOADS
 #define GEMM_AHEAD_STEP0_LOADS 10
@@ -454,46 +458,41 @@ struct NMajorB {
 // Epilogue: the accumulators of one wave to C (fp16, rounded to nearest
 // even) or D (fp32).  smem is the workgroup's LDS of kLds bytes, free once
 // every wave is past the K loop.
-template <class C, bool NN, int kLds>
-__device__ __forceinline__ void store_tile(const typename Mfma<C::MB>::Acc (&acc)[C::FN][C::FM], char *smem,
-                                           const Params &p, int m0, int n0, int wm, int wn, int wave, int lane) {
-    constexpr int TM = C::TM, TN = C::TN, FN = C::FN, MB = C::MB;
-    // MFMA result layout: for 32x32 blocks, lane l register r
-    // holds row 8*(r/4) + 4*(l/32) + r%4, column l%32; for 16x16 blocks,
-    // row 4*(l/16) + r, column l%16.  With the swapped operands the row is n
-    // and the column is m, so each group of 4 registers is 4 consecutive n.
+// Rows of each staging pass for a wave with kWaveBytes of LDS.
+template <class C, bool NN, int kWaveBytes>
+constexpr int staging_rows() {
+    constexpr int RB = C::TN * (NN ? 4 : 2);
+    return C::TM * RB <= kWaveBytes ? C::TM : (C::TM / 2) * RB <= kWaveBytes ? C::TM / 2 : C::TM / 4;
+}
+
+// A wave's TM x TN piece of C on its way out: it goes through LDS in passes
+// of SR rows.  Row r of a pass holds TN outputs (CPR chunks of 16 bytes,
+// chunk c at slot c ^ (r % CPR)); lane l then takes chunk l % CPR of row
+// l / CPR, so CPR consecutive lanes hold one contiguous row segment of C.
+template <class C, bool NN, int kWaveBytes>
+struct CStaging {
+    static constexpr int TM = C::TM, TN = C::TN, FM = C::FM, FN = C::FN, MB = C::MB;
     using Out = std::conditional_t<NN, float, _Float16>;
     using Out4 = std::conditional_t<NN, floatx4, half4>;
-    constexpr int ES = (int)sizeof(Out);
-    constexpr int kGroups = MB == 32 ? 4 : 1;
-    const int frow = lane % MB;
-    const int quad = MB == 32 ? (lane >> 5) * 4 : (lane >> 4) * 4;
-    auto out4 = [&](int j, int i, int g) {
-        Out4 o;
-#pragma unroll
-        for (int e = 0; e < 4; ++e) o[e] = (Out)acc[j][i][4 * g + e];  // fp16: round to nearest even
-        return o;
-    };
+    using Acc = typename Mfma<MB>::Acc;
+    static constexpr int ES = (int)sizeof(Out);
+    static constexpr int kGroups = MB == 32 ? 4 : 1;
+    static constexpr int RB = TN * ES, CPR = RB / 16;
+    static constexpr int SR = staging_rows<C, NN, kWaveBytes>();
+    static constexpr int kPasses = TM / SR;
+    static constexpr int kPerPass = SR * CPR / kWave;  // 16-byte chunks per lane and pass
+    static_assert(SR * RB <= kWaveBytes && SR % MB == 0 && (SR * CPR) % kWave == 0, "staging");
 
-    // Each wave's TM x TN piece goes through LDS in passes of SR rows: row r
-    // of a pass holds TN outputs (CPR chunks of 16 bytes, chunk c at slot
-    // c ^ (r % CPR)); then lane l of a store moves chunk l % CPR of row
-    // l / CPR, so CPR consecutive lanes write one contiguous row segment.
-    constexpr int RB = TN * ES, CPR = RB / 16;
-    constexpr int SR = C::kWaves * TM * RB <= kLds         ? TM
-                       : C::kWaves * (TM / 2) * RB <= kLds ? TM / 2
-                                                            : TM / 4;
-    static_assert(C::kWaves * SR * RB <= kLds && SR % MB == 0 && (SR * CPR) % kWave == 0, "staging");
-    char *const stg = smem + wave * (SR * RB);
-    lds_barrier();  // every wave is done with the operand stages
-    // an opaque zero keeps the staging addresses from being computed before
-    // the K loop, where they would only hold registers
-    int lz;
-    asm volatile("v_mov_b32 %0, 0" : "=v"(lz));
-    const int erow = frow + lz;
-    const bool vec16 = (p.n % (16 / ES)) == 0 && ((uintptr_t)p.c % 16) == 0;
-#pragma unroll
-    for (int pass = 0; pass < TM / SR; ++pass) {
+    // MFMA result layout: for 32x32 blocks, lane l register r holds row
+    // 8*(r/4) + 4*(l/32) + r%4, column l%32; for 16x16 blocks, row
+    // 4*(l/16) + r, column l%16.  With the swapped operands the row is n and
+    // the column is m, so each group of 4 registers is 4 consecutive n.
+    // erow: this lane's row in a block (lane % MB), from an opaque zero so
+    // the staging addresses are not computed early, where they would only
+    // hold registers.
+    static __device__ __forceinline__ void write_pass(const Acc (&acc)[FN][FM], char *stg, int pass, int erow,
+                                                      int lane) {
+        const int quad = MB == 32 ? (lane >> 5) * 4 : (lane >> 4) * 4;
 #pragma unroll
         for (int i = pass * (SR / MB); i < (pass + 1) * (SR / MB); ++i) {
             const int rl = (i - pass * (SR / MB)) * MB + erow;
@@ -501,39 +500,85 @@ __device__ __forceinline__ void store_tile(const typename Mfma<C::MB>::Acc (&acc
             for (int j = 0; j < FN; ++j) {
 #pragma unroll
                 for (int g = 0; g < kGroups; ++g) {
+                    Out4 o;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) o[e] = (Out)acc[j][i][4 * g + e];  // fp16: round to nearest even
                     const int byte = (j * MB + 8 * g + quad) * ES;
-                    *reinterpret_cast<Out4 *>(stg + rl * RB + (((byte >> 4) ^ (rl % CPR)) << 4) + (byte & 15)) =
-                        out4(j, i, g);
+                    *reinterpret_cast<Out4 *>(stg + rl * RB + (((byte >> 4) ^ (rl % CPR)) << 4) + (byte & 15)) = o;
                 }
                 __builtin_amdgcn_sched_barrier(0);
             }
         }
+    }
+
+    static __device__ __forceinline__ int4v read_chunk(const char *stg, int s, int lane) {
+        const int idx = s * kWave + lane;
+        const int r = idx / CPR, c = idx % CPR;
+        return *reinterpret_cast<const int4v *>(stg + r * RB + ((c ^ (r % CPR)) << 4));
+    }
+
+    // chunk s of pass `pass` into C; chunks wholly past N store nothing, only
+    // a chunk that straddles N (or an unaligned C) takes the per-element path
+    static __device__ __forceinline__ void store_chunk(const Params &p, int m0, int n0, int wm, int wn, int pass,
+                                                       int s, int lane, int4v v, bool vec16) {
+        const int idx = s * kWave + lane;
+        const int r = idx / CPR, c = idx % CPR;
+        const int m = m0 + wm * TM + pass * SR + r;
+        const int n = n0 + wn * TN + c * (16 / ES);
+        if (m < p.m && n < p.n) {
+            Out *crow = static_cast<Out *>(p.c) + (int64_t)m * p.n;
+            if (vec16 && n + 16 / ES - 1 < p.n) {
+                *reinterpret_cast<int4v *>(crow + n) = v;
+            } else {
+                union {
+                    int4v v;
+                    Out e[16 / ES];
+                } u;
+                u.v = v;
 #pragma unroll
-        for (int s = 0; s < SR * CPR / kWave; ++s) {
-            const int idx = s * kWave + lane;
-            const int r = idx / CPR, c = idx % CPR;
-            const int4v v = *reinterpret_cast<const int4v *>(stg + r * RB + ((c ^ (r % CPR)) << 4));
-            const int m = m0 + wm * TM + pass * SR + r;
-            const int n = n0 + wn * TN + c * (16 / ES);
-            // chunks wholly past N store nothing; only a chunk that straddles
-            // N (or an unaligned C) takes the per-element path
-            if (m < p.m && n < p.n) {
-                Out *crow = static_cast<Out *>(p.c) + (int64_t)m * p.n;
-                if (vec16 && n + 16 / ES - 1 < p.n) {
-                    *reinterpret_cast<int4v *>(crow + n) = v;
-                } else {
-                    union {
-                        int4v v;
-                        Out e[16 / ES];
-                    } u;
-                    u.v = v;
-#pragma unroll
-                    for (int e = 0; e < 16 / ES; ++e)
-                        if (n + e < p.n) crow[n + e] = u.e[e];
-                }
+                for (int e = 0; e < 16 / ES; ++e)
+                    if (n + e < p.n) crow[n + e] = u.e[e];
             }
         }
     }
+
+    static __device__ __forceinline__ bool vec16(const Params &p) {
+        return (p.n % (16 / ES)) == 0 && ((uintptr_t)p.c % 16) == 0;
+    }
+
+    static __device__ __forceinline__ int opaque_row(int lane) {
+        int lz;
+        asm volatile("v_mov_b32 %0, 0" : "=v"(lz));
+        return lane % MB + lz;
+    }
+};
+
+// The wave's piece of C from its accumulators, staged through kWaveBytes of
+// LDS at stg (the caller makes sure no other wave uses them meanwhile).
+template <class C, bool NN, int kWaveBytes>
+__device__ __forceinline__ void store_tile_at(const typename Mfma<C::MB>::Acc (&acc)[C::FN][C::FM], char *stg,
+                                              const Params &p, int m0, int n0, int wm, int wn, int lane) {
+    using CS = CStaging<C, NN, kWaveBytes>;
+    const int erow = CS::opaque_row(lane);
+    const bool vec16 = CS::vec16(p);
+#pragma unroll
+    for (int pass = 0; pass < CS::kPasses; ++pass) {
+        CS::write_pass(acc, stg, pass, erow, lane);
+#pragma unroll
+        for (int s = 0; s < CS::kPerPass; ++s)
+            CS::store_chunk(p, m0, n0, wm, wn, pass, s, lane, CS::read_chunk(stg, s, lane), vec16);
+    }
+}
+
+// The whole workgroup's C tile, each wave staging through its share of the
+// kLds bytes at smem once every wave is done with the operand stages.
+template <class C, bool NN, int kLds>
+__device__ __forceinline__ void store_tile(const typename Mfma<C::MB>::Acc (&acc)[C::FN][C::FM], char *smem,
+                                           const Params &p, int m0, int n0, int wm, int wn, int wave, int lane) {
+    constexpr int kWaveBytes = kLds / C::kWaves;
+    constexpr int SR = staging_rows<C, NN, kWaveBytes>();
+    lds_barrier();
+    store_tile_at<C, NN, kWaveBytes>(acc, smem + wave * (SR * C::TN * (NN ? 4 : 2)), p, m0, n0, wm, wn, lane);
 }
 
 // Compile-time loop: f(std::integral_constant<int, I>) for I in [B, E).
@@ -845,6 +890,23 @@ struct KMajorDirect {
             t < k_tiles ? rsrc0 : rsrc_none,
             (__attribute__((address_space(3))) void *)(smem + lds_w + S * kStage + i * C::kWaves * 1024), 16,
             vo, (uint32_t)t * 128u, 0, 0);
+    }
+
+    // an opaque copy of the LDS base: the loads' M0 addresses are then
+    // rebuilt where they are used instead of held in scalar registers
+    __device__ __forceinline__ void refresh_lds() { asm volatile("" : "+s"(lds_w)); }
+
+    // load i of K-tile t of the tile whose rows start at base (rows_bytes
+    // of them inside the matrix: the descriptor's range) into stage S
+    template <int S>
+    __device__ __forceinline__ void load_tile(char *smem, const _Float16 *base, uint32_t rows_bytes, int t,
+                                              int i) const {
+        uint32_t vo = voff[i];
+        if constexpr (!KFULL) vo |= (t * C::BK + kc >= k_elems) ? kOutOfRange : 0u;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            make_rsrc(base, rows_bytes),
+            (__attribute__((address_space(3))) void *)(smem + lds_w + S * kStage + i * C::kWaves * 1024), 16, vo,
+            (uint32_t)t * 128u, 0, 0);
     }
 
     __device__ __forceinline__ half8 read(const char *smem, int stage, int ks, int f) const {
@@ -1213,6 +1275,287 @@ void gemm_f16_direct_ahead_kernel(const Params p) {
 
 
 // Fill the output with +0 (K == 0: the zero accumulator is what gets stored).
+// The fragment-ahead kernel with one workgroup per CU walking several tiles
+// (blockIdx.x, + gridDim.x, ...), for square tiles, K a multiple of the
+// K-tile with at least 4 (and an even number of) K-tiles, and C with N % 8
+// == 0 and a 16-byte aligned base.  The K-tile stream runs on across tiles:
+// the last two K-tiles of a tile load the next tile's K-tiles 0 and 1 as
+// their "K-tile t+2"; the last one reads no fragments ahead.  Each wave then
+// stages its C through its share of the LDS beyond the two stages and stores
+// it with 16-byte buffer stores whose out-of-range lanes are dropped by
+// their offsets, so every wave issues exactly kStores of them on every tile.
+// They go out after the loads of the next tile's K-tiles 0 and 1, so the
+// waits that follow (K-tile 0 before its fragment reads, K-tile 1 at the next
+// tile's first acquire barrier) can leave them in flight (the wait counter
+// is in order): the store burst drains under the next tile's MFMAs.
+template <class C>
+__global__ __launch_bounds__(C::kThreads)
+__attribute__((amdgpu_waves_per_eu(C::kMinWavesPerEU, C::kMinWavesPerEU)))
+void gemm_f16_persistent_kernel(const Params p) {
+    constexpr int BM = C::BM, BN = C::BN;
+    constexpr int TM = C::TM, TN = C::TN, FM = C::FM, FN = C::FN;
+    static_assert(C::MB == 16 && C::KS == 2, "two 32-wide k steps per K-tile");
+    static_assert(BM == BN, "stage halves of equal size for the C staging");
+    using OpA = KMajorDirect<C, BM, true>;
+    using OpB = KMajorDirect<C, BN, true>;
+    constexpr int kLdsB = OpA::kLdsBytes;
+    constexpr int kLds = OpA::kLdsBytes + OpB::kLdsBytes;
+    constexpr int LA = OpA::kLoads, L = OpA::kLoads + OpB::kLoads;
+    // LDS beyond the two stages for the C staging: a quarter of a wave's
+    // piece of C per pass, within the 160 KB
+    constexpr int kWaveBytes = (TM / 4 > C::MB ? TM / 4 : C::MB) * TN * 2;
+    constexpr int kSpare = C::kWaves * kWaveBytes;
+    using CS = CStaging<C, false, kWaveBytes>;
+    constexpr int kStores = CS::kPasses * CS::kPerPass;  // 16-byte chunks of a wave's piece of C
+    static_assert(kLds + kSpare <= 160 * 1024, "LDS budget");
+    static_assert(OpA::kStage + (FM - 1) * C::MB * 128 < 65536 && OpB::kStage + (FN - 1) * C::MB * 128 < 65536,
+                  "LDS immediates must fit the 16-bit offset field");
+    __shared__ __attribute__((aligned(1024))) char smem[kLds + kSpare];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int wm = wave / C::WN;
+    const int wn = wave % C::WN;
+
+    const int kt_count = p.k_tiles;  // even, >= 4 (the host's condition)
+    const int ntiles = p.num_m * p.num_n;
+    const int G = gridDim.x;
+    int idx = blockIdx.x;
+
+    // first rows of A, B and C of a tile and the bytes of its rows inside
+    // the matrices (0 past the last tile: loads read zeros)
+    struct TileRows {
+        const _Float16 *a, *b;
+        _Float16 *c;
+        uint32_t a_bytes, b_bytes, c_bytes;
+        int m0, n0;
+    };
+    auto tile_rows = [&](int id) {
+        TileRows r;
+        if (id < ntiles) {
+            const TileCoord tc = tile_coord(id, p.num_m, p.num_n, p.swizzle, p.xcd != 0);
+            r.m0 = (int)tc.m_block * BM;
+            r.n0 = (int)tc.n_block * BN;
+            const uint32_t rows_a = (uint32_t)min(BM, p.m - r.m0), rows_b = (uint32_t)min(BN, p.n - r.n0);
+            r.a = p.a + (int64_t)r.m0 * p.k;
+            r.b = p.b + (int64_t)r.n0 * p.k;
+            r.c = static_cast<_Float16 *>(p.c) + (int64_t)r.m0 * p.n;
+            r.a_bytes = rows_a * (uint32_t)p.k * 2u;
+            r.b_bytes = rows_b * (uint32_t)p.k * 2u;
+            r.c_bytes = rows_a * (uint32_t)p.n * 2u;
+        } else {
+            r.a = p.a;
+            r.b = p.b;
+            r.c = static_cast<_Float16 *>(p.c);
+            r.a_bytes = r.b_bytes = r.c_bytes = 0u;
+            r.m0 = r.n0 = 0;
+        }
+        // wave-uniform by construction; readfirstlane keeps them in scalar
+        // registers through the K loop
+        auto u32 = [](uint32_t v) { return (uint32_t)__builtin_amdgcn_readfirstlane(v); };
+        auto uptr = [&](auto *q) {
+            const uint64_t v = (uint64_t)(uintptr_t)q;
+            return (decltype(q))(uintptr_t)(((uint64_t)u32((uint32_t)(v >> 32)) << 32) | u32((uint32_t)v));
+        };
+        r.a = uptr(r.a);
+        r.b = uptr(r.b);
+        r.c = uptr(r.c);
+        r.a_bytes = u32(r.a_bytes);
+        r.b_bytes = u32(r.b_bytes);
+        r.c_bytes = u32(r.c_bytes);
+        r.m0 = (int)u32((uint32_t)r.m0);
+        r.n0 = (int)u32((uint32_t)r.n0);
+        return r;
+    };
+    TileRows cur = tile_rows(idx);
+    TileRows nxt = tile_rows(idx + G);
+
+    OpA opa;
+    OpB opb;
+    opa.init(cur.a, 0, p.k, kt_count, wave, lane, wm * TM, 0);
+    opb.init(cur.b, 0, p.k, kt_count, wave, lane, wn * TN, kLdsB);
+
+    floatx4 acc[FN][FM];
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int i = 0; i < FM; ++i) acc[j][i] = floatx4{};
+    acc_fence(acc);
+
+    half8 af[3][FM];
+    half8 bf[3][FN];
+    constexpr int NR = FM + FN;  // fragment reads per k step
+    // in the order the MFMAs consume them: B0, A0..A(FM-1), B1..
+    auto read_frag = [&](int buf, int stage, int ks, int r) {
+        if (r == 0)
+            bf[buf][0] = opb.read(smem, stage, ks, 0);
+        else if (r <= FM)
+            af[buf][r - 1] = opa.read(smem, stage, ks, r - 1);
+        else
+            bf[buf][r - FM] = opb.read(smem, stage, ks, r - FM);
+    };
+    // load i of K-tile u of the stream: K-tile u of this tile, or u -
+    // kt_count of the next
+    auto load = [&](auto s_c, int u, int i) {
+        constexpr int S = decltype(s_c)::value;
+        const bool next = u >= kt_count;
+        const int t = next ? u - kt_count : u;
+        if (i < LA)
+            opa.template load_tile<S>(smem, next ? nxt.a : cur.a, next ? nxt.a_bytes : cur.a_bytes, t, i);
+        else
+            opb.template load_tile<S>(smem, next ? nxt.b : cur.b, next ? nxt.b_bytes : cur.b_bytes, t, i - LA);
+    };
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
+    using F = std::false_type;
+    using T = std::true_type;
+    constexpr int NM = FM * FN;
+    constexpr int kRelAt = GEMM_AHEAD_REL_MFMA < NM ? GEMM_AHEAD_REL_MFMA : NM - 1;
+    constexpr int kAcqAt = GEMM_AHEAD_ACQ_MFMA < NM ? GEMM_AHEAD_ACQ_MFMA : NM - 1;
+    constexpr int L0 = L * GEMM_AHEAD_STEP0_LOADS / 16;  // loads of K-tile t+2 in step 0
+    static_assert(L + kStores < 64, "vmcnt range");
+
+    // Prologue: K-tiles 0 and 1 into stages 0 and 1, both in LDS before the
+    // first K-tile (its acquire barrier then waits as after a tile change);
+    // both steps' fragments of K-tile 0 into buffers 0 and 1.
+#pragma unroll
+    for (int i = 0; i < L; ++i) load(S0{}, 0, i);
+#pragma unroll
+    for (int i = 0; i < L; ++i) load(S1{}, 1, i);
+    vm_barrier<0>();
+#pragma unroll
+    for (int r = 0; r < NR; ++r) read_frag(0, 0, 0, r);
+#pragma unroll
+    for (int r = 0; r < NR; ++r) read_frag(1, 0, 1, r);
+
+    // first_c: K-tile 0 of a tile, whose acquire barrier may leave kStores
+    // more operations (the previous tile's stores) in flight.  last_c: the
+    // last K-tile of a tile: its loads, but no fragment reads ahead and so no
+    // acquire barrier.
+    auto k_iter = [&](auto s_c, int t, auto first_c, auto last_c) {
+        constexpr int S = decltype(s_c)::value;
+        constexpr bool FIRST = decltype(first_c)::value;
+        constexpr bool LAST = decltype(last_c)::value;
+        constexpr int SN = S ^ 1;
+        opa.refresh_lds();
+        opb.refresh_lds();
+        constexpr int B1 = S == 0 ? 1 : 2;   // this K-tile's step-1 buffer
+        constexpr int NB1 = S == 0 ? 2 : 1;  // the next K-tile's
+        // step 0
+        static_range<0, NM>([&](auto m_c) {
+            constexpr int m = decltype(m_c)::value;
+            constexpr int j = m / FM, i = (j & 1) ? FM - 1 - m % FM : m % FM;
+            mfma16_tied(bf[0][j], af[0][i], acc[j][i]);
+            if constexpr (m == kRelAt) lgkm_barrier();
+            if constexpr (m >= kRelAt) {
+                constexpr int q = m - kRelAt, slots = NM - kRelAt;
+                static_range<q * L0 / slots, (q + 1) * L0 / slots>(
+                    [&](auto o_c) { load(s_c, t + 2, decltype(o_c)::value); });
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        });
+#pragma unroll
+        for (int j = 0; j < FN; ++j) asm volatile("" ::"v"(bf[0][j]));
+#pragma unroll
+        for (int i = 0; i < FM; ++i) asm volatile("" ::"v"(af[0][i]));
+        // step 1
+        static_range<0, NM>([&](auto m_c) {
+            constexpr int m = decltype(m_c)::value;
+            constexpr int j = m / FM, i = (j & 1) ? FM - 1 - m % FM : m % FM;
+            mfma16_tied(bf[B1][j], af[B1][i], acc[j][i]);
+            if constexpr (!LAST && m == kAcqAt) vm_only_barrier<FIRST ? L0 + kStores : L0>();
+            if constexpr (LAST && m >= kAcqAt) {
+                constexpr int nl = L - L0, slots = NM - kAcqAt, q = m - kAcqAt;
+                static_range<q * nl / slots, (q + 1) * nl / slots>(
+                    [&](auto o_c) { load(s_c, t + 2, L0 + decltype(o_c)::value); });
+            }
+            if constexpr (!LAST && m >= kAcqAt) {
+                constexpr int nl = L - L0, total = 2 * NR + nl, slots = NM - kAcqAt, q = m - kAcqAt;
+                // R R L R R L ...: the reads first while both remain
+                static_range<q * total / slots, (q + 1) * total / slots>([&](auto o_c) {
+                    constexpr int o = decltype(o_c)::value;
+                    constexpr int groups = (2 * NR) / 2 < nl ? (2 * NR) / 2 : nl;  // (R, R, L) groups
+                    constexpr bool in_groups = o < 3 * groups;
+                    constexpr bool is_read = in_groups ? (o % 3 != 2) : (2 * NR > 2 * groups);
+                    constexpr int idx2 = in_groups ? (is_read ? (o / 3) * 2 + (o % 3) : o / 3)
+                                                   : (is_read ? 2 * groups + (o - 3 * groups) : groups + (o - 3 * groups));
+                    if constexpr (is_read) {
+                        constexpr int ks = idx2 / NR, r = idx2 % NR;
+                        read_frag(ks == 0 ? 0 : NB1, SN, ks, r);
+                    } else {
+                        load(s_c, t + 2, L0 + idx2);
+                    }
+                });
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        });
+#pragma unroll
+        for (int j = 0; j < FN; ++j) asm volatile("" ::"v"(bf[B1][j]));
+#pragma unroll
+        for (int i = 0; i < FM; ++i) asm volatile("" ::"v"(af[B1][i]));
+    };
+
+    for (;;) {
+        k_iter(S0{}, 0, T{}, F{});
+        k_iter(S1{}, 1, F{}, F{});
+        int kt = 2;
+        for (; kt + 2 < kt_count; kt += 2) {
+            k_iter(S0{}, kt, F{}, F{});
+            k_iter(S1{}, kt + 1, F{}, F{});
+        }
+        k_iter(S0{}, kt, F{}, F{});
+        k_iter(S1{}, kt + 1, F{}, T{});
+        // C through this wave's staging area (no other wave uses it, and its
+        // own last reads of it were a tile ago), each 16-byte chunk stored as
+        // it is read back: a chunk past N gets an out-of-range offset, rows
+        // past M lie beyond the descriptor's range.
+        acc_fence(acc);
+        {
+            char *const stg = smem + kLds + wave * kWaveBytes;
+            const __amdgpu_buffer_rsrc_t rc = make_rsrc(cur.c, cur.c_bytes);
+            // an opaque zero: the staging and store addresses are computed
+            // here, not kept live through the K loop as loop invariants
+            int lz;
+            asm volatile("v_mov_b32 %0, 0" : "=v"(lz));
+            const int el = lane + lz;
+            const int erow = el % C::MB;
+#pragma unroll
+            for (int pass = 0; pass < CS::kPasses; ++pass) {
+                CS::write_pass(acc, stg, pass, erow, el);
+#pragma unroll
+                for (int q = 0; q < CS::kPerPass; ++q) {
+                    const int e = q * kWave + el;
+                    const int r = wm * TM + pass * CS::SR + e / CS::CPR;  // row inside the tile
+                    const int n = cur.n0 + wn * TN + (e % CS::CPR) * 8;
+                    const uint32_t off = (n < p.n) ? (uint32_t)(r * p.n + n) * 2u : kOutOfRange;
+                    __builtin_amdgcn_raw_buffer_store_b128(CS::read_chunk(stg, q, el), rc, off, 0, 0);
+                    __builtin_amdgcn_sched_barrier(0);  // one chunk at a time: few live registers
+                }
+            }
+        }
+        if (idx + G >= ntiles) break;
+        // The next tile's K-tile 0 (loaded before its K-tile 1 and the
+        // stores) is in LDS for every wave: its fragments into buffers 0, 1.
+        vm_only_barrier<L + kStores>();
+#pragma unroll
+        for (int r = 0; r < NR; ++r) read_frag(0, 0, 0, r);
+#pragma unroll
+        for (int r = 0; r < NR; ++r) read_frag(1, 0, 1, r);
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+#pragma unroll
+            for (int i = 0; i < FM; ++i) acc[j][i] = floatx4{};
+        acc_fence(acc);
+        idx += G;
+        cur = nxt;
+        nxt = tile_rows(idx + G);
+    }
+    // the last tile's loads past the tile (zeros into LDS) are done before
+    // the workgroup ends
+    __builtin_amdgcn_s_waitcnt(0);
+}
+
 template <class T>
 __global__ __launch_bounds__(256) void fill_zero_kernel(T *c, int64_t count) {
     const int64_t stride = (int64_t)gridDim.x * blockDim.x;
@@ -1300,6 +1643,19 @@ static bool ranges_overlap(const void *p, int64_t pb, const void *q, int64_t qb)
     return pb > 0 && qb > 0 && a0 < b1 && b0 < a1;
 }
 
+// Compute units of the current device (0 if unknown), cached per device.
+static int device_cus() {
+    static int cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    if (cached[dev] == 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) return 0;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
+
 // gfx950 check, cached per device.
 static int check_device() {
     static int cached[64];  // 0 = unknown, 1 = gfx950, -1 = other
@@ -1328,6 +1684,17 @@ static void launch(const Params &p, int g, hipStream_t stream) {
             const dim3 block(CD::kThreads);
             const bool full = p.k % CD::BK == 0;
             if constexpr (GEMM_AHEAD && CD::MB == 16) {
+                // more tiles than CUs: one workgroup per CU walking several
+                // tiles, where its conditions hold
+                if constexpr (CD::BM == CD::BN) {
+                    const int64_t tiles = (int64_t)p.num_m * p.num_n;
+                    const int cus = GEMM_PERSIST ? device_cus() : 0;
+                    if (full && p.k_tiles % 2 == 0 && p.k_tiles >= 4 && cus > 0 && tiles > cus && p.n % 8 == 0 &&
+                        ((uintptr_t)p.c % 16) == 0 && (int64_t)CD::BM * p.n * 2 < (int64_t(1) << 31)) {
+                        hipLaunchKernelGGL((gemm_f16_persistent_kernel<CD>), dim3((unsigned)cus), block, 0, stream, p);
+                        return;
+                    }
+                }
                 if (full) hipLaunchKernelGGL((gemm_f16_direct_ahead_kernel<CD, true>), grid, block, 0, stream, p);
                 else hipLaunchKernelGGL((gemm_f16_direct_ahead_kernel<CD, false>), grid, block, 0, stream, p);
             } else {
