@@ -1276,8 +1276,8 @@ void gemm_f16_direct_ahead_kernel(const Params p) {
 
 // Fill the output with +0 (K == 0: the zero accumulator is what gets stored).
 // The fragment-ahead kernel with one workgroup per CU walking several tiles
-// (blockIdx.x, + gridDim.x, ...), for square tiles, K a multiple of the
-// K-tile with at least 4 (and an even number of) K-tiles, and C with N % 8
+// (blockIdx.x, + gridDim.x, ...), for K a multiple of the K-tile with at
+// least 4 (and an even number of) K-tiles, and C with N % 8
 // == 0 and a 16-byte aligned base.  The K-tile stream runs on across tiles:
 // the last two K-tiles of a tile load the next tile's K-tiles 0 and 1 as
 // their "K-tile t+2"; the last one reads no fragments ahead.  Each wave then
@@ -1295,7 +1295,6 @@ void gemm_f16_persistent_kernel(const Params p) {
     constexpr int BM = C::BM, BN = C::BN;
     constexpr int TM = C::TM, TN = C::TN, FM = C::FM, FN = C::FN;
     static_assert(C::MB == 16 && C::KS == 2, "two 32-wide k steps per K-tile");
-    static_assert(BM == BN, "stage halves of equal size for the C staging");
     using OpA = KMajorDirect<C, BM, true>;
     using OpB = KMajorDirect<C, BN, true>;
     constexpr int kLdsB = OpA::kLdsBytes;
@@ -1686,7 +1685,7 @@ static void launch(const Params &p, int g, hipStream_t stream) {
             if constexpr (GEMM_AHEAD && CD::MB == 16) {
                 // more tiles than CUs: one workgroup per CU walking several
                 // tiles, where its conditions hold
-                if constexpr (CD::BM == CD::BN) {
+                {
                     const int64_t tiles = (int64_t)p.num_m * p.num_n;
                     const int cus = GEMM_PERSIST ? device_cus() : 0;
                     if (full && p.k_tiles % 2 == 0 && p.k_tiles >= 4 && cus > 0 && tiles > cus && p.n % 8 == 0 &&

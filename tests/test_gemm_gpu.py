@@ -211,12 +211,13 @@ def test_direct_to_lds_path_bit_exact(m, n, k, tile):
     assert_bits_equal(run_gemm(a, b, tile=tile), oracle.gemm_f16_nt(a, b), f"{m}x{n}x{k}")
 
 
-# More block tiles than CUs on a square tile, K a multiple of the K-tile with
+# More block tiles than CUs, K a multiple of the K-tile with
 # an even count of at least 4, 16-byte aligned C with N % 8 == 0: one
 # workgroup per CU walks several tiles and the K-tile stream runs across the
 # tile changes.  Ragged last tiles in M and N; 1 to 5 tiles per workgroup.
 PERSISTENT = [(g.TILE_64x64, 1100, 1064, 256), (g.TILE_64x64, 2100, 2104, 256),
-              (g.TILE_128x128, 2100, 2088, 384), (g.TILE_256x256, 4200, 4152, 512)]
+              (g.TILE_128x128, 2100, 2088, 384), (g.TILE_256x256, 4200, 4152, 512),
+              (g.TILE_256x128, 4200, 2088, 256), (g.TILE_128x256, 2100, 4152, 256)]
 
 
 @pytest.mark.parametrize("tile,m,n,k", PERSISTENT)
