@@ -914,6 +914,110 @@ struct KMajorDirect {
     }
 };
 
+typedef __fp16 fp16x4 __attribute__((__vector_size__(4 * sizeof(__fp16))));
+typedef __attribute__((address_space(3))) fp16x4 lds_fp16x4;
+
+// ds_read_b64_tr_b16 through a restrict pointer.  The alias scope that the
+// restrict parameter gives the read keeps the compiler from waiting for every
+// direct-to-LDS load in flight (vmcnt 0) before it, which it does for a read
+// it cannot tell apart from them; the kernels order these reads after the
+// loads that fill their stage with their own waits and barriers, as they do
+// for plain LDS reads.
+static __device__ __forceinline__ fp16x4 lds_read_tr16(lds_fp16x4 *__restrict__ p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4f16(p);
+}
+
+// B of the second contract ([K, N] row-major) for 16x16x32 tiles, loaded
+// straight into LDS.  Stage: the K-tile as 64 k-rows of BN fp16, unpadded
+// (a direct load fills 1 KB, 1024 / (2 BN) whole k-rows); the 16-byte chunk
+// c of k-row r sits at slot c ^ sw(r), sw(r) = 2 ((r & 3) | ((r >> 1) & 4)).
+// A 16x16x32 fragment needs 8 consecutive k of one column per lane: two
+// ds_read_b64_tr_b16 give it (in each 16-lane group, lane j reads 4
+// consecutive n of k-row j / 4 and the hardware hands lane i the 4 k values
+// of column i); a half-wave of such a read touches 8 k-rows, r and r + 8
+// among them, whose 32-byte segments the swizzle puts on distinct banks.
+// The swizzle of a lane's rows is the same in every k step (rows differ by
+// multiples of 4 and by 8 g), but not additive across fragments, so each
+// fragment column has its own address register.  Rows past K lie beyond
+// the K-tile's descriptor; chunks past N (N % 8 == 0) get an out-of-range
+// offset.
+template <class C, bool KFULL>
+struct NMajorDirect {
+    static constexpr int BN = C::BN, BK = C::BK, FN = C::FN;
+    static constexpr int CPR = BN / 8;  // 16-byte chunks per k-row
+    static constexpr int kRowB = BN * 2;
+    static constexpr int kStage = BK * kRowB;
+    static constexpr int kLdsBytes = 2 * kStage;
+    static constexpr int kRowsPerBlock = 1024 / kRowB;
+    static constexpr int kBlocks = kStage / 1024;
+    static constexpr int kLoads = kBlocks / C::kWaves;  // per wave and K-tile
+    static_assert(C::MB == 16 && C::KS == 2 && BK == 64, "16x16x32 fragments of a 64-wide K-tile");
+    static_assert(CPR >= 16 && CPR <= 64, "the swizzle needs 16..64 chunks per k-row");
+    static_assert(kBlocks % C::kWaves == 0, "whole blocks per wave");
+
+    static __device__ __forceinline__ int sw(int r) { return 2 * ((r & 3) | ((r >> 1) & 4)); }
+
+    uint32_t voff[kLoads];  // this lane's chunk in its rows of the K-tile, bit 31 set past N
+    const _Float16 *b;  // B + n0: column n0 of k-row 0
+    int n_total, k_elems, k_tiles, n0;
+    int lds_w;        // this wave's first block of stage 0
+    int r_lane[FN];   // fragment f, k step 0, first half, stage 0
+
+    __device__ __forceinline__ void init(const _Float16 *bmat, int n_first, int N, int K, int kt_count, int wave,
+                                         int lane, int frag_col, int lds) {
+        // the tile's columns start at b; uniform values pinned to scalar registers
+        const uint64_t addr = (uint64_t)(uintptr_t)(bmat + n_first);
+        const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)addr);
+        const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(addr >> 32));
+        b = (const _Float16 *)(uintptr_t)(((uint64_t)hi << 32) | lo);
+        n_total = __builtin_amdgcn_readfirstlane(N);
+        k_elems = K;
+        k_tiles = kt_count;
+        n0 = __builtin_amdgcn_readfirstlane(n_first);
+#pragma unroll
+        for (int i = 0; i < kLoads; ++i) {
+            const int r = (i * C::kWaves + wave) * kRowsPerBlock + lane / CPR;
+            const int c = (lane % CPR) ^ sw(r);
+            voff[i] = ((uint32_t)(r * N + c * 8) * 2u) | ((n0 + c * 8 >= N) ? kOutOfRange : 0u);
+        }
+        lds_w = lds + wave * 1024;
+        const int g = lane >> 4, j = lane & 15;
+        const int row = 8 * g + (j >> 2);     // + 32 ks + 4 h
+        const int fsw = sw(row) >> 1;         // the same for every ks, h
+#pragma unroll
+        for (int f = 0; f < FN; ++f)
+            r_lane[f] = lds + row * kRowB + ((((frag_col >> 4) + f) ^ fsw) << 5) + (((j >> 1) & 1) << 4) +
+                        ((j & 1) << 3);
+    }
+
+    // load i of K-tile t into stage S: k-rows t BK .. of columns n0 ..
+    template <int S>
+    __device__ __forceinline__ void load(char *smem, int t, int i) const {
+        // past the last K-tile: an empty range at the last one's base
+        const bool live = t < k_tiles;
+        const int k0 = (live ? t : k_tiles - 1) * BK;
+        const uint32_t bytes = live ? (uint32_t)(min(BK, k_elems - k0) * n_total - n0) * 2u : 0u;
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            make_rsrc(b + (int64_t)k0 * n_total, bytes),
+            (__attribute__((address_space(3))) void *)(smem + lds_w + S * kStage + i * C::kWaves * 1024), 16,
+            voff[i], 0, 0, 0);
+    }
+
+    __device__ __forceinline__ half8 read(const char *smem, int stage, int ks, int f) const {
+        char *p0 = const_cast<char *>(smem) + r_lane[f] + stage * kStage + ks * 32 * kRowB;
+        // address-space casts of pointers into the __shared__ array
+        const fp16x4 lo = lds_read_tr16((lds_fp16x4 *)p0);
+        const fp16x4 hi = lds_read_tr16((lds_fp16x4 *)(p0 + 4 * kRowB));
+        half8 r;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            r[e] = (_Float16)lo[e];
+            r[4 + e] = (_Float16)hi[e];
+        }
+        return r;
+    }
+};
+
 // Orders every accumulator after a stretch of s_nop: all accesses of acc
 // before the call happen before the nops, all after it after them.  24 wait
 // states cover the MFMA result latency (the hazards between an
@@ -1124,7 +1228,7 @@ __device__ __forceinline__ void vm_only_barrier() {
 // instead of a burst after one barrier, and the last of them still have a k
 // step to land.  Fragments rotate over three register buffers: step 0 always
 // uses buffer 0, step 1 uses buffer 1 on stage 0 and buffer 2 on stage 1.
-template <class C, bool KFULL>
+template <class C, bool KFULL, bool NN>
 __global__ __launch_bounds__(C::kThreads)
 __attribute__((amdgpu_waves_per_eu(C::kMinWavesPerEU, C::kMinWavesPerEU)))
 void gemm_f16_direct_ahead_kernel(const Params p) {
@@ -1132,13 +1236,14 @@ void gemm_f16_direct_ahead_kernel(const Params p) {
     constexpr int TM = C::TM, TN = C::TN, FM = C::FM, FN = C::FN;
     static_assert(C::MB == 16 && C::KS == 2, "two 32-wide k steps per K-tile");
     using OpA = KMajorDirect<C, BM, KFULL>;
-    using OpB = KMajorDirect<C, BN, KFULL>;
+    using OpB = std::conditional_t<NN, NMajorDirect<C, KFULL>, KMajorDirect<C, BN, KFULL>>;
     constexpr int kLdsB = OpA::kLdsBytes;
     constexpr int kLds = OpA::kLdsBytes + OpB::kLdsBytes;
     constexpr int LA = OpA::kLoads, L = OpA::kLoads + OpB::kLoads;
     static_assert(kLds <= 160 * 1024, "LDS budget");
     static_assert(2 * L < 64, "vmcnt range");
-    static_assert(OpA::kStage + (FM - 1) * C::MB * 128 < 65536 && OpB::kStage + (FN - 1) * C::MB * 128 < 65536,
+    static_assert(OpA::kStage + (FM - 1) * C::MB * 128 < 65536 && OpB::kStage + (FN - 1) * C::MB * 128 < 65536 &&
+                      OpB::kStage + 36 * (BN * 2) < 65536,
                   "LDS immediates must fit the 16-bit offset field");
     __shared__ __attribute__((aligned(1024))) char smem[kLds];
 
@@ -1157,7 +1262,10 @@ void gemm_f16_direct_ahead_kernel(const Params p) {
     OpA opa;
     OpB opb;
     opa.init(p.a + (int64_t)m0 * p.k, min(BM, p.m - m0), p.k, kt_count, wave, lane, wm * TM, 0);
-    opb.init(p.b + (int64_t)n0 * p.k, min(BN, p.n - n0), p.k, kt_count, wave, lane, wn * TN, kLdsB);
+    if constexpr (NN)
+        opb.init(p.b, n0, p.n, p.k, kt_count, wave, lane, wn * TN, kLdsB);
+    else
+        opb.init(p.b + (int64_t)n0 * p.k, min(BN, p.n - n0), p.k, kt_count, wave, lane, wn * TN, kLdsB);
 
     floatx4 acc[FN][FM];
 #pragma unroll
@@ -1270,7 +1378,7 @@ void gemm_f16_direct_ahead_kernel(const Params p) {
 
     vm_barrier<0>();  // no load is still writing LDS when the epilogue stages C there
     acc_fence(acc);
-    store_tile<C, false, kLds>(acc, smem, p, m0, n0, wm, wn, wave, lane);
+    store_tile<C, NN, kLds>(acc, smem, p, m0, n0, wm, wn, wave, lane);
 }
 
 
@@ -1678,6 +1786,16 @@ template <class C, bool NN, class CD = C>
 static void launch(const Params &p, int g, hipStream_t stream) {
     static_assert(CD::BM == C::BM && CD::BN == C::BN, "one block tile");
     const dim3 grid((unsigned)((int64_t)p.num_m * p.num_n));
+    if constexpr (NN && GEMM_DIRECT && GEMM_AHEAD && CD::MB == 16 && CD::BN >= 128) {
+        // B [K,N] straight into LDS: 16-byte chunks of a k-row, a K-tile's
+        // byte offsets below 2^31
+        if (g == 8 && (int64_t)CD::BK * p.n * 2 < (int64_t(1) << 31)) {
+            const dim3 block(CD::kThreads);
+            if (p.k % CD::BK == 0) hipLaunchKernelGGL((gemm_f16_direct_ahead_kernel<CD, true, true>), grid, block, 0, stream, p);
+            else hipLaunchKernelGGL((gemm_f16_direct_ahead_kernel<CD, false, true>), grid, block, 0, stream, p);
+            return;
+        }
+    }
     if constexpr (!NN && GEMM_DIRECT) {
         if (g == 8) {
             const dim3 block(CD::kThreads);
@@ -1694,8 +1812,8 @@ static void launch(const Params &p, int g, hipStream_t stream) {
                         return;
                     }
                 }
-                if (full) hipLaunchKernelGGL((gemm_f16_direct_ahead_kernel<CD, true>), grid, block, 0, stream, p);
-                else hipLaunchKernelGGL((gemm_f16_direct_ahead_kernel<CD, false>), grid, block, 0, stream, p);
+                if (full) hipLaunchKernelGGL((gemm_f16_direct_ahead_kernel<CD, true, false>), grid, block, 0, stream, p);
+                else hipLaunchKernelGGL((gemm_f16_direct_ahead_kernel<CD, false, false>), grid, block, 0, stream, p);
             } else {
                 if (full) hipLaunchKernelGGL((gemm_f16_direct_kernel<CD, true>), grid, block, 0, stream, p);
                 else hipLaunchKernelGGL((gemm_f16_direct_kernel<CD, false>), grid, block, 0, stream, p);

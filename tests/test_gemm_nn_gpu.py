@@ -123,6 +123,26 @@ def test_ragged_shapes(m, n, k, tile):
     assert_fp32_bound(run_nn(a, b, tile=tile), d64, dabs, k, f"{m}x{n}x{k}")
 
 
+# K and N multiples of 8 on the 16x16x32 tiles: B [K,N] goes straight into
+# LDS by k-rows and is read back transposed.  Odd and even K-tile counts, a
+# last K-tile of 8..56 k, N ragged by 8 past a tile, a single 8-wide column
+# chunk, several tiles in both directions.
+NN_DIRECT = [(1, 8, 8), (64, 128, 64), (300, 264, 200), (129, 520, 72), (513, 1032, 520), (257, 392, 1000),
+             (70, 136, 8), (1000, 776, 1088)]
+NN_DIRECT_TILES = [t for t in NN_TILES if t != g.TILE_256x256_W8 and t != g.TILE_64x64]
+
+
+@pytest.mark.parametrize("m,n,k", NN_DIRECT)
+@pytest.mark.parametrize("tile", NN_DIRECT_TILES)
+def test_direct_to_lds_b_path_bit_exact(m, n, k, tile):
+    _announce("nn direct", m, n, k, tile)
+    rng = np.random.default_rng(m * 7 + n * 11 + k + tile)
+    a = (rng.integers(-8, 9, size=(m, k)) / 8).astype(np.float16)
+    b = (rng.integers(-8, 9, size=(k, n)) / 8).astype(np.float16)
+    d64, _ = oracle.gemm_f16_nn_f64(a, b)
+    assert_exact(run_nn(a, b, tile=tile), d64, f"{m}x{n}x{k}")
+
+
 @pytest.mark.parametrize("m,n,k", [(70, 13, 40), (33, 100, 24), (64, 21, 19)])
 def test_n_or_k_not_multiple_of_8_takes_the_scalar_loaders(m, n, k):
     _announce("nn scalar", m, n, k)
