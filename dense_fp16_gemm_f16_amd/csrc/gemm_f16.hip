@@ -462,7 +462,10 @@ struct NMajorB {
 template <class C, bool NN, int kWaveBytes>
 constexpr int staging_rows() {
     constexpr int RB = C::TN * (NN ? 4 : 2);
-    return C::TM * RB <= kWaveBytes ? C::TM : (C::TM / 2) * RB <= kWaveBytes ? C::TM / 2 : C::TM / 4;
+    return C::TM * RB <= kWaveBytes         ? C::TM
+           : (C::TM / 2) * RB <= kWaveBytes ? C::TM / 2
+           : (C::TM / 4) * RB <= kWaveBytes ? C::TM / 4
+                                            : C::TM / 8;
 }
 
 // A wave's TM x TN piece of C on its way out: it goes through LDS in passes
@@ -957,8 +960,12 @@ struct NMajorDirect {
 
     static __device__ __forceinline__ int sw(int r) { return 2 * ((r & 3) | ((r >> 1) & 4)); }
 
+    // loads i and i + 2 take the same chunk of their rows (rows 16 apart)
+    static_assert((2 * C::kWaves * kRowsPerBlock) % 16 == 0, "chunk index periodic in the load index");
+
     uint32_t voff[kLoads];  // this lane's chunk in its rows of the K-tile, bit 31 set past N
-    const _Float16 *b;  // B + n0: column n0 of k-row 0
+    int ccol[2];            // column of that chunk in the tile, loads of even / odd index
+    const _Float16 *b;      // B + n0: column n0 of k-row 0
     int n_total, k_elems, k_tiles, n0;
     int lds_w;        // this wave's first block of stage 0
     int r_lane[FN];   // fragment f, k step 0, first half, stage 0
@@ -979,6 +986,7 @@ struct NMajorDirect {
             const int r = (i * C::kWaves + wave) * kRowsPerBlock + lane / CPR;
             const int c = (lane % CPR) ^ sw(r);
             voff[i] = ((uint32_t)(r * N + c * 8) * 2u) | ((n0 + c * 8 >= N) ? kOutOfRange : 0u);
+            if (i < 2) ccol[i] = c * 8;
         }
         lds_w = lds + wave * 1024;
         const int g = lane >> 4, j = lane & 15;
@@ -1001,6 +1009,23 @@ struct NMajorDirect {
             make_rsrc(b + (int64_t)k0 * n_total, bytes),
             (__attribute__((address_space(3))) void *)(smem + lds_w + S * kStage + i * C::kWaves * 1024), 16,
             voff[i], 0, 0, 0);
+    }
+
+    // an opaque copy of the LDS base (see KMajorDirect::refresh_lds)
+    __device__ __forceinline__ void refresh_lds() { asm volatile("" : "+s"(lds_w)); }
+
+    // load i of K-tile t (whole: K % BK == 0) of the tile whose columns
+    // start at tile_b = B + tile_n0; bytes: the range of a K-tile from there
+    // (0: the loads read zeros).  The offsets were masked for columns past N
+    // from column 0 in init; this adds the tile's own mask.
+    template <int S>
+    __device__ __forceinline__ void load_tile(char *smem, const _Float16 *tile_b, int tile_n0, uint32_t bytes, int t,
+                                              int i) const {
+        const uint32_t vo = voff[i] | ((tile_n0 + ccol[i & 1] >= n_total) ? kOutOfRange : 0u);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            make_rsrc(tile_b + (int64_t)t * BK * n_total, bytes),
+            (__attribute__((address_space(3))) void *)(smem + lds_w + S * kStage + i * C::kWaves * 1024), 16, vo, 0,
+            0, 0);
     }
 
     __device__ __forceinline__ half8 read(const char *smem, int stage, int ks, int f) const {
@@ -1386,7 +1411,7 @@ void gemm_f16_direct_ahead_kernel(const Params p) {
 // The fragment-ahead kernel with one workgroup per CU walking several tiles
 // (blockIdx.x, + gridDim.x, ...), for K a multiple of the K-tile with at
 // least 4 (and an even number of) K-tiles, and C with N % 8
-// == 0 and a 16-byte aligned base.  The K-tile stream runs on across tiles:
+// == 0 and a 16-byte aligned base; NN: B [K,N] and D fp32.  The K-tile stream runs on across tiles:
 // the last two K-tiles of a tile load the next tile's K-tiles 0 and 1 as
 // their "K-tile t+2"; the last one reads no fragments ahead.  Each wave then
 // stages its C through its share of the LDS beyond the two stages and stores
@@ -1396,7 +1421,7 @@ void gemm_f16_direct_ahead_kernel(const Params p) {
 // waits that follow (K-tile 0 before its fragment reads, K-tile 1 at the next
 // tile's first acquire barrier) can leave them in flight (the wait counter
 // is in order): the store burst drains under the next tile's MFMAs.
-template <class C>
+template <class C, bool NN>
 __global__ __launch_bounds__(C::kThreads)
 __attribute__((amdgpu_waves_per_eu(C::kMinWavesPerEU, C::kMinWavesPerEU)))
 void gemm_f16_persistent_kernel(const Params p) {
@@ -1404,18 +1429,24 @@ void gemm_f16_persistent_kernel(const Params p) {
     constexpr int TM = C::TM, TN = C::TN, FM = C::FM, FN = C::FN;
     static_assert(C::MB == 16 && C::KS == 2, "two 32-wide k steps per K-tile");
     using OpA = KMajorDirect<C, BM, true>;
-    using OpB = KMajorDirect<C, BN, true>;
+    using OpB = std::conditional_t<NN, NMajorDirect<C, true>, KMajorDirect<C, BN, true>>;
     constexpr int kLdsB = OpA::kLdsBytes;
     constexpr int kLds = OpA::kLdsBytes + OpB::kLdsBytes;
     constexpr int LA = OpA::kLoads, L = OpA::kLoads + OpB::kLoads;
-    // LDS beyond the two stages for the C staging: a quarter of a wave's
-    // piece of C per pass, within the 160 KB
-    constexpr int kWaveBytes = (TM / 4 > C::MB ? TM / 4 : C::MB) * TN * 2;
+    // LDS beyond the two stages for the C staging: a quarter (fp16) or an
+    // eighth (fp32) of a wave's piece of C per pass, within the 160 KB
+    constexpr int ES = NN ? 4 : 2;
+    constexpr int kPassRows = TM * 2 / (4 * ES) > C::MB ? TM * 2 / (4 * ES) : C::MB;
+    constexpr int kWaveBytes = kPassRows * TN * ES;
     constexpr int kSpare = C::kWaves * kWaveBytes;
-    using CS = CStaging<C, false, kWaveBytes>;
+    using CS = CStaging<C, NN, kWaveBytes>;
     constexpr int kStores = CS::kPasses * CS::kPerPass;  // 16-byte chunks of a wave's piece of C
+    // a wait may leave at most 63 operations in flight: past that it waits
+    // for some of the stores as well
+    constexpr int kLeave = L + kStores < 63 ? L + kStores : 63;
     static_assert(kLds + kSpare <= 160 * 1024, "LDS budget");
-    static_assert(OpA::kStage + (FM - 1) * C::MB * 128 < 65536 && OpB::kStage + (FN - 1) * C::MB * 128 < 65536,
+    static_assert(OpA::kStage + (FM - 1) * C::MB * 128 < 65536 && OpB::kStage + (FN - 1) * C::MB * 128 < 65536 &&
+                      OpB::kStage + 36 * (BN * 2) < 65536,
                   "LDS immediates must fit the 16-bit offset field");
     __shared__ __attribute__((aligned(1024))) char smem[kLds + kSpare];
 
@@ -1434,7 +1465,7 @@ void gemm_f16_persistent_kernel(const Params p) {
     // the matrices (0 past the last tile: loads read zeros)
     struct TileRows {
         const _Float16 *a, *b;
-        _Float16 *c;
+        char *c;
         uint32_t a_bytes, b_bytes, c_bytes;
         int m0, n0;
     };
@@ -1446,15 +1477,20 @@ void gemm_f16_persistent_kernel(const Params p) {
             r.n0 = (int)tc.n_block * BN;
             const uint32_t rows_a = (uint32_t)min(BM, p.m - r.m0), rows_b = (uint32_t)min(BN, p.n - r.n0);
             r.a = p.a + (int64_t)r.m0 * p.k;
-            r.b = p.b + (int64_t)r.n0 * p.k;
-            r.c = static_cast<_Float16 *>(p.c) + (int64_t)r.m0 * p.n;
+            r.c = static_cast<char *>(p.c) + (int64_t)r.m0 * p.n * ES;
             r.a_bytes = rows_a * (uint32_t)p.k * 2u;
-            r.b_bytes = rows_b * (uint32_t)p.k * 2u;
-            r.c_bytes = rows_a * (uint32_t)p.n * 2u;
+            r.c_bytes = rows_a * (uint32_t)p.n * (uint32_t)ES;
+            if constexpr (NN) {  // B [K,N]: columns n0.. of a K-tile's k-rows
+                r.b = p.b + r.n0;
+                r.b_bytes = (uint32_t)(C::BK * p.n - r.n0) * 2u;
+            } else {
+                r.b = p.b + (int64_t)r.n0 * p.k;
+                r.b_bytes = rows_b * (uint32_t)p.k * 2u;
+            }
         } else {
             r.a = p.a;
             r.b = p.b;
-            r.c = static_cast<_Float16 *>(p.c);
+            r.c = static_cast<char *>(p.c);
             r.a_bytes = r.b_bytes = r.c_bytes = 0u;
             r.m0 = r.n0 = 0;
         }
@@ -1481,7 +1517,10 @@ void gemm_f16_persistent_kernel(const Params p) {
     OpA opa;
     OpB opb;
     opa.init(cur.a, 0, p.k, kt_count, wave, lane, wm * TM, 0);
-    opb.init(cur.b, 0, p.k, kt_count, wave, lane, wn * TN, kLdsB);
+    if constexpr (NN)
+        opb.init(p.b, 0, p.n, p.k, kt_count, wave, lane, wn * TN, kLdsB);
+    else
+        opb.init(cur.b, 0, p.k, kt_count, wave, lane, wn * TN, kLdsB);
 
     floatx4 acc[FN][FM];
 #pragma unroll
@@ -1510,6 +1549,9 @@ void gemm_f16_persistent_kernel(const Params p) {
         const int t = next ? u - kt_count : u;
         if (i < LA)
             opa.template load_tile<S>(smem, next ? nxt.a : cur.a, next ? nxt.a_bytes : cur.a_bytes, t, i);
+        else if constexpr (NN)
+            opb.template load_tile<S>(smem, next ? nxt.b : cur.b, next ? nxt.n0 : cur.n0,
+                                      next ? nxt.b_bytes : cur.b_bytes, t, i - LA);
         else
             opb.template load_tile<S>(smem, next ? nxt.b : cur.b, next ? nxt.b_bytes : cur.b_bytes, t, i - LA);
     };
@@ -1521,7 +1563,7 @@ void gemm_f16_persistent_kernel(const Params p) {
     constexpr int kRelAt = GEMM_AHEAD_REL_MFMA < NM ? GEMM_AHEAD_REL_MFMA : NM - 1;
     constexpr int kAcqAt = GEMM_AHEAD_ACQ_MFMA < NM ? GEMM_AHEAD_ACQ_MFMA : NM - 1;
     constexpr int L0 = L * GEMM_AHEAD_STEP0_LOADS / 16;  // loads of K-tile t+2 in step 0
-    static_assert(L + kStores < 64, "vmcnt range");
+    constexpr int kLeave0 = L0 + kStores < 63 ? L0 + kStores : 63;
 
     // Prologue: K-tiles 0 and 1 into stages 0 and 1, both in LDS before the
     // first K-tile (its acquire barrier then waits as after a tile change);
@@ -1571,7 +1613,7 @@ void gemm_f16_persistent_kernel(const Params p) {
             constexpr int m = decltype(m_c)::value;
             constexpr int j = m / FM, i = (j & 1) ? FM - 1 - m % FM : m % FM;
             mfma16_tied(bf[B1][j], af[B1][i], acc[j][i]);
-            if constexpr (!LAST && m == kAcqAt) vm_only_barrier<FIRST ? L0 + kStores : L0>();
+            if constexpr (!LAST && m == kAcqAt) vm_only_barrier<FIRST ? kLeave0 : L0>();
             if constexpr (LAST && m >= kAcqAt) {
                 constexpr int nl = L - L0, slots = NM - kAcqAt, q = m - kAcqAt;
                 static_range<q * nl / slots, (q + 1) * nl / slots>(
@@ -1634,8 +1676,8 @@ void gemm_f16_persistent_kernel(const Params p) {
                 for (int q = 0; q < CS::kPerPass; ++q) {
                     const int e = q * kWave + el;
                     const int r = wm * TM + pass * CS::SR + e / CS::CPR;  // row inside the tile
-                    const int n = cur.n0 + wn * TN + (e % CS::CPR) * 8;
-                    const uint32_t off = (n < p.n) ? (uint32_t)(r * p.n + n) * 2u : kOutOfRange;
+                    const int n = cur.n0 + wn * TN + (e % CS::CPR) * (16 / ES);
+                    const uint32_t off = (n < p.n) ? (uint32_t)(r * p.n + n) * (uint32_t)ES : kOutOfRange;
                     __builtin_amdgcn_raw_buffer_store_b128(CS::read_chunk(stg, q, el), rc, off, 0, 0);
                     __builtin_amdgcn_sched_barrier(0);  // one chunk at a time: few live registers
                 }
@@ -1644,7 +1686,7 @@ void gemm_f16_persistent_kernel(const Params p) {
         if (idx + G >= ntiles) break;
         // The next tile's K-tile 0 (loaded before its K-tile 1 and the
         // stores) is in LDS for every wave: its fragments into buffers 0, 1.
-        vm_only_barrier<L + kStores>();
+        vm_only_barrier<kLeave>();
 #pragma unroll
         for (int r = 0; r < NR; ++r) read_frag(0, 0, 0, r);
 #pragma unroll
@@ -1791,7 +1833,15 @@ static void launch(const Params &p, int g, hipStream_t stream) {
         // byte offsets below 2^31
         if (g == 8 && (int64_t)CD::BK * p.n * 2 < (int64_t(1) << 31)) {
             const dim3 block(CD::kThreads);
-            if (p.k % CD::BK == 0) hipLaunchKernelGGL((gemm_f16_direct_ahead_kernel<CD, true, true>), grid, block, 0, stream, p);
+            const bool full = p.k % CD::BK == 0;
+            const int64_t tiles = (int64_t)p.num_m * p.num_n;
+            const int cus = GEMM_PERSIST ? device_cus() : 0;
+            if (full && p.k_tiles % 2 == 0 && p.k_tiles >= 4 && cus > 0 && tiles > cus && ((uintptr_t)p.c % 16) == 0 &&
+                (int64_t)CD::BM * p.n * 4 < (int64_t(1) << 31)) {
+                hipLaunchKernelGGL((gemm_f16_persistent_kernel<CD, true>), dim3((unsigned)cus), block, 0, stream, p);
+                return;
+            }
+            if (full) hipLaunchKernelGGL((gemm_f16_direct_ahead_kernel<CD, true, true>), grid, block, 0, stream, p);
             else hipLaunchKernelGGL((gemm_f16_direct_ahead_kernel<CD, false, true>), grid, block, 0, stream, p);
             return;
         }
@@ -1808,7 +1858,7 @@ static void launch(const Params &p, int g, hipStream_t stream) {
                     const int cus = GEMM_PERSIST ? device_cus() : 0;
                     if (full && p.k_tiles % 2 == 0 && p.k_tiles >= 4 && cus > 0 && tiles > cus && p.n % 8 == 0 &&
                         ((uintptr_t)p.c % 16) == 0 && (int64_t)CD::BM * p.n * 2 < (int64_t(1) << 31)) {
-                        hipLaunchKernelGGL((gemm_f16_persistent_kernel<CD>), dim3((unsigned)cus), block, 0, stream, p);
+                        hipLaunchKernelGGL((gemm_f16_persistent_kernel<CD, false>), dim3((unsigned)cus), block, 0, stream, p);
                         return;
                     }
                 }

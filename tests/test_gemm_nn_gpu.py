@@ -143,6 +143,24 @@ def test_direct_to_lds_b_path_bit_exact(m, n, k, tile):
     assert_exact(run_nn(a, b, tile=tile), d64, f"{m}x{n}x{k}")
 
 
+# More tiles than CUs, K a multiple of 64 with an even K-tile count >= 4:
+# one workgroup per CU walking tiles, the next tile's K-tiles 0 and 1 loaded
+# under the current one's last two, D staged in eighths of a wave's piece.
+# Ragged M and N (by 8..56 past a tile) on every 16x16x32 tile.
+NN_PERSISTENT = [(g.TILE_128x128, 2100, 2088, 384), (g.TILE_256x256, 4200, 4152, 512),
+                 (g.TILE_256x128, 4200, 2088, 256), (g.TILE_128x256, 2100, 4152, 256)]
+
+
+@pytest.mark.parametrize("tile,m,n,k", NN_PERSISTENT)
+def test_persistent_path_bit_exact(tile, m, n, k):
+    _announce("nn persistent", tile, m, n, k)
+    rng = np.random.default_rng(m + n + k + tile)
+    a = (rng.integers(-8, 9, size=(m, k)) / 8).astype(np.float16)
+    b = (rng.integers(-8, 9, size=(k, n)) / 8).astype(np.float16)
+    d64, _ = oracle.gemm_f16_nn_f64(a, b)
+    assert_exact(run_nn(a, b, tile=tile), d64, f"{m}x{n}x{k}")
+
+
 @pytest.mark.parametrize("m,n,k", [(70, 13, 40), (33, 100, 24), (64, 21, 19)])
 def test_n_or_k_not_multiple_of_8_takes_the_scalar_loaders(m, n, k):
     _announce("nn scalar", m, n, k)
