@@ -1458,6 +1458,7 @@ void gemm_f16_persistent_kernel(const Params p) {
 
     const int kt_count = p.k_tiles;  // even, >= 4 (the host's condition)
     const int ntiles = p.num_m * p.num_n;
+    const bool c_lines = (p.n * ES) % 128 == 0 && ((uintptr_t)p.c % 128) == 0;
     const int G = gridDim.x;
     int idx = blockIdx.x;
 
@@ -1678,7 +1679,14 @@ void gemm_f16_persistent_kernel(const Params p) {
                     const int r = wm * TM + pass * CS::SR + e / CS::CPR;  // row inside the tile
                     const int n = cur.n0 + wn * TN + (e % CS::CPR) * (16 / ES);
                     const uint32_t off = (n < p.n) ? (uint32_t)(r * p.n + n) * (uint32_t)ES : kOutOfRange;
-                    __builtin_amdgcn_raw_buffer_store_b128(CS::read_chunk(stg, q, el), rc, off, 0, 0);
+                    // rows of whole 128-byte lines: streaming (nt) stores, which keep the
+                    // C lines from displacing the A and B lines that other workgroups of
+                    // the XCD still read from L2; on rows that end inside a line they were
+                    // measured slower, so those keep the default policy
+                    if (c_lines)
+                        __builtin_amdgcn_raw_buffer_store_b128(CS::read_chunk(stg, q, el), rc, off, 0, 2);
+                    else
+                        __builtin_amdgcn_raw_buffer_store_b128(CS::read_chunk(stg, q, el), rc, off, 0, 0);
                     __builtin_amdgcn_sched_barrier(0);  // one chunk at a time: few live registers
                 }
             }
