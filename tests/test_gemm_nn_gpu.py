@@ -146,9 +146,11 @@ def test_direct_to_lds_b_path_bit_exact(m, n, k, tile):
 # More tiles than CUs, K a multiple of 64 with an even K-tile count >= 4:
 # one workgroup per CU walking tiles, the next tile's K-tiles 0 and 1 loaded
 # under the current one's last two, D staged in eighths of a wave's piece.
-# Ragged M and N (by 8..56 past a tile) on every 16x16x32 tile.
+# Ragged M and N (by 8..64 past a tile) on every 16x16x32 tile; N % 32 == 0
+# (fp32 rows of whole 128-byte lines) takes the non-temporal stores.
 NN_PERSISTENT = [(g.TILE_128x128, 2100, 2088, 384), (g.TILE_256x256, 4200, 4152, 512),
-                 (g.TILE_256x128, 4200, 2088, 256), (g.TILE_128x256, 2100, 4152, 256)]
+                 (g.TILE_256x128, 4200, 2088, 256), (g.TILE_128x256, 2100, 4152, 256),
+                 (g.TILE_256x256, 4200, 4128, 256), (g.TILE_128x256, 2100, 4160, 256)]
 
 
 @pytest.mark.parametrize("tile,m,n,k", NN_PERSISTENT)
