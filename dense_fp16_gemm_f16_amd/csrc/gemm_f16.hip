@@ -1791,6 +1791,10 @@ static int check_sizes(int64_t m, int64_t n, int64_t k) {
     if (m < 0 || n < 0 || k < 0) return GEMM_F16_EINVAL;
     if (m >= (int64_t(1) << 31) || n >= (int64_t(1) << 31)) return GEMM_F16_EINVAL;
     if (k >= (int64_t(1) << 22)) return GEMM_F16_EINVAL;
+    // m, n < 2^31, so the product cannot overflow; the bound keeps every
+    // byte extent (m*n*4, m*k*2, n*k*2) far below 2^63 and the address range
+    // checks free of wrap-around
+    if (m * n >= (int64_t(1) << 47)) return GEMM_F16_EINVAL;
     return GEMM_F16_OK;
 }
 
