@@ -1789,9 +1789,11 @@ static int auto_tile(int64_t m, int64_t n) {
 
 static int check_sizes(int64_t m, int64_t n, int64_t k) {
     if (m < 0 || n < 0 || k < 0) return GEMM_F16_EINVAL;
-    if (m >= (int64_t(1) << 31) || n >= (int64_t(1) << 31)) return GEMM_F16_EINVAL;
+    // The kernels index rows and columns of C in 32-bit ints, and the last
+    // block tile reaches up to 255 past m and n: below 2^30 that cannot wrap.
+    if (m >= (int64_t(1) << 30) || n >= (int64_t(1) << 30)) return GEMM_F16_EINVAL;
     if (k >= (int64_t(1) << 22)) return GEMM_F16_EINVAL;
-    // m, n < 2^31, so the product cannot overflow; the bound keeps every
+    // m, n < 2^30, so the product cannot overflow; the bound keeps every
     // byte extent (m*n*4, m*k*2, n*k*2) far below 2^63 and the address range
     // checks free of wrap-around
     if (m * n >= (int64_t(1) << 47)) return GEMM_F16_EINVAL;

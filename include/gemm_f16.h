@@ -42,7 +42,7 @@ extern "C" {
 
 enum {
     GEMM_F16_OK = 0,
-    GEMM_F16_EINVAL = -1,     /* negative size, M or N >= 2^31, M*N >= 2^47, K >= 2^22, bad option */
+    GEMM_F16_EINVAL = -1,     /* negative size, M or N >= 2^30, M*N >= 2^47, K >= 2^22, bad option */
     GEMM_F16_ENULL = -2,      /* null pointer with a non-empty extent */
     GEMM_F16_EALIGN = -3,     /* pointer not aligned to its element size (2 or 4 bytes) */
     GEMM_F16_EDEVICE = -4,    /* current device is not gfx950 */
@@ -53,7 +53,7 @@ enum {
 /*
  * C = fp16(A * B^T) with fp32 accumulation (see the top of this file).
  *
- * m, n, k >= 0; m, n < 2^31; m*n < 2^47; k < 2^22.
+ * m, n, k >= 0; m, n < 2^30; m*n < 2^47; k < 2^22.
  * m == 0 or n == 0: returns GEMM_F16_OK and launches nothing.
  * k == 0: C is filled with +0 (the zero accumulator is stored).
  * Sizes that are not multiples of the block tile are handled: elements of A

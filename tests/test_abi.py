@@ -70,6 +70,8 @@ FAKE_A, FAKE_B, FAKE_C = 0x10000000, 0x20000000, 0x30000000  # never dereference
         ((4, 4, -1, FAKE_A, FAKE_B, FAKE_C), g.EINVAL),
         ((4, 4, 1 << 22, FAKE_A, FAKE_B, FAKE_C), g.EINVAL),
         ((1 << 31, 4, 4, FAKE_A, FAKE_B, FAKE_C), g.EINVAL),
+        ((1 << 30, 4, 4, FAKE_A, FAKE_B, FAKE_C), g.EINVAL),
+        ((4, 1 << 30, 4, FAKE_A, FAKE_B, FAKE_C), g.EINVAL),
         ((1 << 24, 1 << 23, 4, FAKE_A, FAKE_B, FAKE_C), g.EINVAL),
         ((4, 4, 4, 0, FAKE_B, FAKE_C), g.ENULL),
         ((4, 4, 4, FAKE_A, 0, FAKE_C), g.ENULL),

@@ -231,6 +231,57 @@ def test_persistent_path_bit_exact(tile, m, n, k):
     assert_bits_equal(run_gemm(a, b, tile=tile), oracle.gemm_f16_nt(a, b), f"{m}x{n}x{k}")
 
 
+# The largest K the library takes (K < 2^22): a 64x64 output, so the oracle
+# stays cheap, on the direct path (K % 64 == 0, the automatic 64x64 tile and
+# the 256x256 tile, whose operand ranges are then 256 rows x K x 2 bytes, just
+# below 2^31) and on the element loader (K odd).  Entries from {-1, 0, 1}:
+# every partial sum is an integer of magnitude below 2^22 < 2^24, exact in
+# fp32 in any order, so the one fp16 rounding is unique and the bar is
+# bit-exact.
+MAX_K = [((1 << 22) - 64, g.TILE_AUTO), ((1 << 22) - 64, g.TILE_256x256), ((1 << 22) - 1, g.TILE_AUTO)]
+
+
+@pytest.mark.parametrize("k,tile", MAX_K)
+def test_largest_k_bit_exact(k, tile):
+    _announce("max-k", k, tile)
+    rng = np.random.default_rng(k + tile)
+    a = rng.integers(-1, 2, size=(64, k), dtype=np.int8).astype(np.float16)
+    b = rng.integers(-1, 2, size=(64, k), dtype=np.int8).astype(np.float16)
+    assert_bits_equal(run_gemm(a, b, tile=tile), oracle.gemm_f16_nt(a, b), f"64x64x{k}")
+
+
+# C rows of nearly 2^22 columns: with N = 2^22 - 8 a 256-row block of C still
+# spans less than 2^31 bytes and the one-workgroup-per-CU kernel takes the
+# shape (32768 tiles); with N = 2^22 it does not, and the one-tile-per-workgroup
+# kernel does.  A has one 1 per row, at column p(m), so C[m][n] = B[n][p(m)]
+# exactly (one non-zero product, exact in fp32, and an fp16 value needs no
+# rounding): the check runs on the GPU over all of C, with guard bands.
+@pytest.mark.parametrize("n", [(1 << 22) - 8, 1 << 22])
+def test_widest_rows_one_hot(n):
+    _announce("wide-n", n)
+    m, k = 512, 256
+    dev = torch.device("cuda")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(n)
+    b = torch.randn((n, k), generator=gen, device=dev).to(torch.float16)
+    tiny = b.abs() < 2.0**-10  # keep clear of fp16 subnormals, as normal_f16 does
+    b = torch.where(tiny, torch.copysign(torch.full_like(b, 2.0**-10), b), b)
+    p = (torch.arange(m, device=dev) * 37 + 11) % k
+    a = torch.zeros((m, k), dtype=torch.float16, device=dev)
+    a[torch.arange(m, device=dev), p] = 1.0
+    c_buf = torch.full((GUARD + m * n + GUARD,), SENTINEL, dtype=torch.int16, device=dev)
+    rc = g.gemm_f16_nt_raw(m, n, k, a.data_ptr(), b.data_ptr(), c_buf.data_ptr() + 2 * GUARD,
+                           torch.cuda.current_stream().cuda_stream)
+    assert rc == g.OK, g.status_string(rc)
+    torch.cuda.synchronize()
+    assert bool((c_buf[:GUARD] == SENTINEL).all()) and bool((c_buf[GUARD + m * n:] == SENTINEL).all()), \
+        "write outside C"
+    c = c_buf[GUARD:GUARD + m * n].view(m, n)
+    expect = b[:, p].t().contiguous().view(torch.int16)
+    bad = int((c != expect).sum())
+    assert bad == 0, f"{m}x{n}x{k} one-hot: {bad} mismatches"
+
+
 @pytest.mark.parametrize("a_off,b_off", [(1, 0), (0, 3), (5, 7)])
 def test_unaligned_operands_take_the_scalar_loader(a_off, b_off):
     _announce("unaligned", a_off, b_off)
