@@ -15,6 +15,9 @@ Workloads (shapes and value distributions):
 * ``gemm_16384x4096x2048_normal05``  i.i.d. N(0, 0.5) read as standard
   deviation 0.5, rounded to fp16.
 * ``gemm_5000x3000x1000_eighths``    ragged, {-8..8}/8 through the same LCG.
+* ``gemm_1024x8192x8192_uniform``    one GPU's share of the 8192^3 GEMM when
+  eight GPUs split M (each takes 1024 rows of A and C and all of B),
+  uniform[-1,1] with its own seed.
 
 The float distributions use numpy's PCG64 generator in float32 and round to
 fp16 with numpy's round-to-nearest-even conversion.
@@ -58,6 +61,7 @@ WORKLOADS = {
         Workload("gemm_8192_uniform", 8192, 8192, 8192, "uniform", 8192),
         Workload("gemm_16384x4096x2048_normal05", 16384, 4096, 2048, "normal05", 2048),
         Workload("gemm_5000x3000x1000_eighths", 5000, 3000, 1000, "eighths", LCG_SEED),
+        Workload("gemm_1024x8192x8192_uniform", 1024, 8192, 8192, "uniform", 1024),
         Workload("gemm_nn_256_eighths", 256, 256, 256, "eighths", LCG_SEED, "kn"),
         Workload("gemm_nn_5000x3000x1000_eighths", 5000, 3000, 1000, "eighths", LCG_SEED, "kn"),
         Workload("gemm_nn_8192_uniform", 8192, 8192, 8192, "uniform", 8192, "kn"),

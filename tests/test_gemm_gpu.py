@@ -139,7 +139,8 @@ def _rows_one_per_tile(m, bm=256):
     return sorted(rows)
 
 
-@pytest.mark.parametrize("name", ["gemm_8192_uniform", "gemm_16384x4096x2048_normal05"])
+@pytest.mark.parametrize("name", ["gemm_8192_uniform", "gemm_16384x4096x2048_normal05",
+                                  "gemm_1024x8192x8192_uniform"])
 def test_large_workloads_sampled_rows(name):
     """Full-size runs in the default launch configuration; the oracle computes
     one row per 256-row block tile (all N columns, full K)."""
