@@ -181,6 +181,40 @@ def test_k_zero_and_empty():
     assert run_nn(np.zeros((0, 8), np.float16), np.ones((8, 16), np.float16)).shape == (0, 16)
 
 
+# Rows of B (and D) near the column limits of the second contract's kernels:
+# a 256-row block of fp32 D spans less than 2^31 bytes below N = 2^21 (the
+# one-workgroup-per-CU kernel takes 2^21 - 8, the one-tile-per-workgroup
+# kernel 2^21), and a K-tile's 64 k-rows of B do below N = 2^24 (the
+# direct-to-LDS loader takes 2^24 - 8, the register-staged one 2^24).  A has
+# one 1 per row, at column p(m), so D[m][n] = B[p(m)][n] exactly; the check
+# runs on the GPU over all of D, with guard bands.
+WIDE_NN = [(512, (1 << 21) - 8, 256), (512, 1 << 21, 256), (64, (1 << 24) - 8, 64), (64, 1 << 24, 64)]
+
+
+@pytest.mark.parametrize("m,n,k", WIDE_NN)
+def test_widest_rows_one_hot(m, n, k):
+    _announce("nn wide-n", m, n, k)
+    dev = torch.device("cuda")
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(n + k)
+    b = torch.randn((k, n), generator=gen, device=dev).to(torch.float16)
+    tiny = b.abs() < 2.0**-10  # keep clear of fp16 subnormals
+    b = torch.where(tiny, torch.copysign(torch.full_like(b, 2.0**-10), b), b)
+    p = (torch.arange(m, device=dev) * 37 + 11) % k
+    a = torch.zeros((m, k), dtype=torch.float16, device=dev)
+    a[torch.arange(m, device=dev), p] = 1.0
+    d_buf = torch.full((GUARD + m * n + GUARD,), float(SENTINEL), dtype=torch.float32, device=dev)
+    rc = g.gemm_f16_nn_f32_raw(m, n, k, a.data_ptr(), b.data_ptr(), d_buf.data_ptr() + 4 * GUARD,
+                               torch.cuda.current_stream().cuda_stream)
+    assert rc == g.OK, g.status_string(rc)
+    torch.cuda.synchronize()
+    assert bool((d_buf[:GUARD] == float(SENTINEL)).all()) and \
+        bool((d_buf[GUARD + m * n:] == float(SENTINEL)).all()), "write outside D"
+    d = d_buf[GUARD:GUARD + m * n].view(m, n)
+    bad = int((d.view(torch.int32) != b[p, :].float().view(torch.int32)).sum())
+    assert bad == 0, f"{m}x{n}x{k} one-hot: {bad} mismatches"
+
+
 def test_8192_uniform_sampled_rows():
     """The measurement workload of this contract, default launch; the oracle
     computes one row per 256-row block tile."""
