@@ -283,6 +283,59 @@ def test_widest_rows_one_hot(n):
     assert bad == 0, f"{m}x{n}x{k} one-hot: {bad} mismatches"
 
 
+# The epilogue's cast at the top of the fp16 range: a sum of 65520 or more
+# rounds to infinity (65520 is the midpoint between the largest finite value,
+# 65504, and 2^16, and ties go to the even neighbour, 2^16), 65519 rounds
+# down to 65504.  Every sum here is an integer below 2^24, exact in fp32 in
+# any order, so the rounded result is unique and the bar is bit-exact.
+@pytest.mark.parametrize("tile", TILES)
+def test_epilogue_overflow_bit_exact(tile):
+    _announce("overflow", tile)
+    rng = np.random.default_rng(65520 + tile)
+    m, n, k = 70, 90, 40
+    a = np.zeros((m, k), np.float64)
+    b = np.zeros((n, k), np.float64)
+    a[:, 0], a[:, 1] = 256.0, 1.0
+    b[:, 0] = 255.875  # 256 * 255.875 = 65504, the largest finite fp16
+    b[:, 1] = rng.integers(-20, 21, size=n)  # 65504 + t for t in [-20, 20]
+    sign = np.where(rng.random(m) < 0.5, -1.0, 1.0)
+    a[:, 0] *= sign
+    a[:, 1] *= sign
+    a[:, 2] = rng.integers(0, 3, size=m)  # plus 0, 64 or 128 more on some rows
+    b[:, 2] = 64.0
+    a, b = a.astype(np.float16), b.astype(np.float16)
+    ref = oracle.gemm_f16_nt(a, b)
+    assert np.isinf(ref.astype(np.float32)).any() and (np.abs(ref.astype(np.float32)) == 65504).any()
+    assert_bits_equal(run_gemm(a, b, tile=tile), ref, f"overflow tile {tile}")
+
+
+# Non-finite operands: +-inf times a non-zero value gives +-inf, inf times 0
+# and inf - inf give NaN, and NaN propagates.  NaN payloads and signs are not
+# fixed by the arithmetic, so NaN is compared as a class; every other
+# element bit for bit.
+@pytest.mark.parametrize("tile", TILES)
+def test_non_finite_operands(tile):
+    _announce("non-finite", tile)
+    rng = np.random.default_rng(7 + tile)
+    m, n, k = 66, 72, 24
+    a = (rng.integers(-8, 9, size=(m, k)) / 8).astype(np.float16)
+    b = (rng.integers(-8, 9, size=(n, k)) / 8).astype(np.float16)
+    b[:, 0] = np.where(rng.random(n) < 0.2, 0.0, b[:, 0])
+    a[0, 0] = np.inf
+    a[1, 0] = -np.inf
+    a[2, 0], a[2, 1] = np.inf, -np.inf
+    a[3, 5] = np.nan
+    b[4, 7] = np.inf
+    ref = oracle.gemm_f16_nt(a, b)
+    got = run_gemm(a, b, tile=tile)
+    rn, gn = np.isnan(ref.astype(np.float32)), np.isnan(got.astype(np.float32))
+    assert rn.any() and np.isinf(ref.astype(np.float32)).any()
+    bad = np.argwhere(rn != gn)
+    assert bad.size == 0, f"NaN pattern differs at {tuple(bad[0])}: gpu {got[tuple(bad[0])]} oracle {ref[tuple(bad[0])]}"
+    keep = ~rn
+    assert np.array_equal(got.view(np.uint16)[keep], ref.view(np.uint16)[keep]), "finite/inf elements differ"
+
+
 @pytest.mark.parametrize("a_off,b_off", [(1, 0), (0, 3), (5, 7)])
 def test_unaligned_operands_take_the_scalar_loader(a_off, b_off):
     _announce("unaligned", a_off, b_off)

@@ -215,6 +215,32 @@ def test_widest_rows_one_hot(m, n, k):
     assert bad == 0, f"{m}x{n}x{k} one-hot: {bad} mismatches"
 
 
+# Non-finite operands: +-inf times a non-zero value gives +-inf, inf times 0
+# and inf - inf give NaN, and NaN propagates.  NaN is compared as a class;
+# every other element exactly ({-8..8}/8 elsewhere: exact sums).
+@pytest.mark.parametrize("tile", NN_TILES)
+def test_non_finite_operands(tile):
+    _announce("nn non-finite", tile)
+    rng = np.random.default_rng(11 + tile)
+    m, n, k = 66, 72, 24
+    a = (rng.integers(-8, 9, size=(m, k)) / 8).astype(np.float16)
+    b = (rng.integers(-8, 9, size=(k, n)) / 8).astype(np.float16)
+    b[0, :] = np.where(rng.random(n) < 0.2, 0.0, b[0, :])
+    a[0, 0] = np.inf
+    a[1, 0] = -np.inf
+    a[2, 0], a[2, 1] = np.inf, -np.inf
+    a[3, 5] = np.nan
+    b[7, 4] = np.inf
+    with np.errstate(invalid="ignore"):
+        d64, _ = oracle.gemm_f16_nn_f64(a, b)
+    got = run_nn(a, b, tile=tile)
+    rn, gn = np.isnan(d64), np.isnan(got)
+    assert rn.any() and np.isinf(d64).any()
+    bad = np.argwhere(rn != gn)
+    assert bad.size == 0, f"NaN pattern differs at {tuple(bad[0])}: gpu {got[tuple(bad[0])]} ref {d64[tuple(bad[0])]}"
+    assert np.array_equal(got[~rn].astype(np.float64), d64[~rn]), "finite/inf elements differ"
+
+
 def test_8192_uniform_sampled_rows():
     """The measurement workload of this contract, default launch; the oracle
     computes one row per 256-row block tile."""
