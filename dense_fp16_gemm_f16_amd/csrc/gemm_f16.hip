@@ -37,6 +37,7 @@
 // The sum of each output runs over K-tiles in increasing order, and inside
 // a K-tile over 16-wide k steps in increasing order, whatever the grid
 // order: results do not depend on the rasterization options.
+#include <atomic>
 #include <hip/hip_runtime.h>
 
 #include <stdint.h>
@@ -1341,7 +1342,6 @@ void gemm_f16_direct_ahead_kernel(const Params p) {
     auto k_iter = [&](auto s_c, int t) {
         constexpr int S = decltype(s_c)::value;
         constexpr int SN = S ^ 1;
-        using SNc = std::integral_constant<int, SN>;
         constexpr int B1 = S == 0 ? 1 : 2;   // this K-tile's step-1 buffer
         constexpr int NB1 = S == 0 ? 2 : 1;  // the next K-tile's
         // step 0
@@ -1806,34 +1806,40 @@ static bool ranges_overlap(const void *p, int64_t pb, const void *q, int64_t qb)
     return pb > 0 && qb > 0 && a0 < b1 && b0 < a1;
 }
 
+// Per-device caches below: host threads may call the library at the same
+// time, so the entries are atomics; a first call on a device in two threads
+// at once computes the same value twice and stores it twice.
+
 // Compute units of the current device (0 if unknown), cached per device.
 static int device_cus() {
-    static int cached[64];
+    static std::atomic<int> cached[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-    if (cached[dev] == 0) {
-        int n = 0;
+    int n = cached[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
         if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) return 0;
-        cached[dev] = n;
+        cached[dev].store(n, std::memory_order_relaxed);
     }
-    return cached[dev];
+    return n;
 }
 
 // gfx950 check, cached per device.
 static int check_device() {
-    static int cached[64];  // 0 = unknown, 1 = gfx950, -1 = other
+    static std::atomic<int> cached[64];  // 0 = unknown, 1 = gfx950, -1 = other
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess) return GEMM_F16_EHIP;
     if (dev < 0 || dev >= 64) return GEMM_F16_EDEVICE;
-    if (cached[dev] == 0) {
+    int state = cached[dev].load(std::memory_order_relaxed);
+    if (state == 0) {
         hipDeviceProp_t prop;
         if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return GEMM_F16_EHIP;
         const char *arch = prop.gcnArchName;
         const bool ok = arch[0] == 'g' && arch[1] == 'f' && arch[2] == 'x' && arch[3] == '9' &&
                         arch[4] == '5' && arch[5] == '0' && (arch[6] == '\0' || arch[6] == ':');
-        cached[dev] = ok ? 1 : -1;
+        state = ok ? 1 : -1;
+        cached[dev].store(state, std::memory_order_relaxed);
     }
-    return cached[dev] == 1 ? GEMM_F16_OK : GEMM_F16_EDEVICE;
+    return state == 1 ? GEMM_F16_OK : GEMM_F16_EDEVICE;
 }
 
 // CD: the configuration of the direct-to-LDS kernel (C = A B^T, 16-byte

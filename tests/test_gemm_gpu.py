@@ -336,6 +336,43 @@ def test_non_finite_operands(tile):
     assert np.array_equal(got.view(np.uint16)[keep], ref.view(np.uint16)[keep]), "finite/inf elements differ"
 
 
+def test_concurrent_host_threads():
+    """Eight host threads call the C ABI at once (ctypes releases the GIL for
+    the call), each on its own stream, from a fresh start of nothing: every
+    result must match the oracle bit for bit."""
+    import threading
+
+    _announce("threads")
+    rng = np.random.default_rng(31)
+    m, n, k = 300, 270, 200
+    a = (rng.integers(-8, 9, size=(m, k)) / 8).astype(np.float16)
+    b = (rng.integers(-8, 9, size=(n, k)) / 8).astype(np.float16)
+    ref = oracle.gemm_f16_nt(a, b)
+    dev = torch.device("cuda")
+    a_d, b_d = torch.from_numpy(a).to(dev), torch.from_numpy(b).to(dev)
+    outs = [torch.empty((m, n), dtype=torch.float16, device=dev) for _ in range(8)]
+    streams = [torch.cuda.Stream() for _ in range(8)]  # default priority
+    codes = [None] * 8
+    torch.cuda.synchronize()
+
+    def work(i):
+        rc = g.OK
+        for _ in range(5):
+            rc = rc or g.gemm_f16_nt_raw(m, n, k, a_d.data_ptr(), b_d.data_ptr(), outs[i].data_ptr(),
+                                         streams[i].cuda_stream, tile=1 + i % 7)
+        codes[i] = rc
+
+    threads = [threading.Thread(target=work, args=(i,)) for i in range(8)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    torch.cuda.synchronize()
+    assert codes == [g.OK] * 8, codes
+    for i, o in enumerate(outs):
+        assert_bits_equal(o.cpu().numpy(), ref, f"thread {i}")
+
+
 @pytest.mark.parametrize("a_off,b_off", [(1, 0), (0, 3), (5, 7)])
 def test_unaligned_operands_take_the_scalar_loader(a_off, b_off):
     _announce("unaligned", a_off, b_off)
