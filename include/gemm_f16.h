@@ -26,6 +26,10 @@
  * void*; NULL is the null stream) and the call returns without waiting.
  * Completion is the caller's business (stream or event synchronisation).
  *
+ * Threads: every entry point may be called from several host threads at
+ * once.  The only state the library keeps is a per-device cache of the
+ * device's architecture and compute-unit count, filled on first use.
+ *
  * Errors: every entry point returns 0 on success or one of the negative
  * GEMM_F16_E* codes below; gemm_f16_status_string() names them.  Argument
  * checks run before any HIP call, so an invalid call has no effect.  The
