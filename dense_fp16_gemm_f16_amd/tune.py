@@ -3,6 +3,7 @@
     python -m dense_fp16_gemm_f16_amd.tune [--shapes M,N,K ...] [--rounds 3]
     python -m dense_fp16_gemm_f16_amd.tune --data      # operand values vs time
     python -m dense_fp16_gemm_f16_amd.tune --ceiling   # MFMA rate, no HBM traffic
+    python -m dense_fp16_gemm_f16_amd.tune --graph 100 # eager launches vs one HIP graph
 
 For every shape (default: the five benchmark workloads) it times each block
 tile (and, for the default tile, a few swizzle widths) with HIP events,
@@ -34,9 +35,14 @@ def main(argv=None) -> int:
     ap.add_argument("--ceiling", action="store_true",
                     help="instead: the sustained v_mfma_f32_32x32x16_f16 and v_mfma_f32_16x16x32_f16 rates of the device with no "
                          "global memory traffic (libmfma_ceiling.so), on random and on zero operands")
+    ap.add_argument("--graph", type=int, default=0, metavar="N",
+                    help="instead: time N GEMMs of each shape (default 256^3, 1024^3, 2048^3) launched "
+                         "eagerly and replayed from one captured HIP graph")
     a = ap.parse_args(argv)
     import torch
 
+    if a.graph:
+        return graph_sweep(a, torch)
     if a.data:
         return data_sweep(a, torch)
     if a.ceiling:
@@ -121,6 +127,58 @@ def data_sweep(a, torch) -> int:
         us = statistics.median(t) * 1e3
         print(json.dumps({"shape": [m, n, k], "operands": name, "us": round(us, 1),
                           "tflops": round(2.0 * m * n * k / (us * 1e-6) / 1e12, 1)}), flush=True)
+    return 0
+
+
+def graph_sweep(a, torch) -> int:
+    """Launch-bound shapes: N back-to-back GEMMs enqueued one call at a time,
+    against the same N GEMMs captured once in a HIP graph and replayed.  Both
+    are timed with one HIP-event pair around all N; the result is per GEMM."""
+    shapes = ([tuple(int(x) for x in s.split(",")) for s in a.shapes] if a.shapes else
+              [(256, 256, 256), (1024, 1024, 1024), (2048, 2048, 2048)])
+    gen = torch.Generator(device="cuda").manual_seed(3)
+    n_gemm = a.graph
+    for (m, n, k) in shapes:
+        A = (torch.rand((m, k), device="cuda", generator=gen) * 2 - 1).half()
+        B = (torch.rand((n, k), device="cuda", generator=gen) * 2 - 1).half()
+        C = torch.empty((m, n), device="cuda", dtype=torch.float16)
+        side = torch.cuda.Stream()  # default priority
+
+        def enqueue(stream):
+            for _ in range(n_gemm):
+                rc = g.gemm_f16_nt_raw(m, n, k, A.data_ptr(), B.data_ptr(), C.data_ptr(), stream.cuda_stream)
+                if rc != g.OK:
+                    raise g.GemmError(rc)
+
+        with torch.cuda.stream(side):
+            enqueue(side)  # warm-up, outside any capture
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(side):
+            with torch.cuda.graph(graph, stream=side):
+                enqueue(torch.cuda.current_stream())
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        res = {"eager": [], "graph": []}
+        for _ in range(max(a.rounds, 3)):
+            for mode in ("eager", "graph"):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                with torch.cuda.stream(side):
+                    e0.record(side)
+                    if mode == "eager":
+                        enqueue(side)
+                    else:
+                        graph.replay()
+                    e1.record(side)
+                torch.cuda.synchronize()
+                res[mode].append(e0.elapsed_time(e1) * 1e3 / n_gemm)
+        for mode, t in res.items():
+            us = statistics.median(t)
+            print(json.dumps({"shape": [m, n, k], "mode": mode, "gemms": n_gemm, "tile": g.select_tile(m, n, k),
+                              "us_per_gemm": round(us, 2), "tflops": round(2.0 * m * n * k / (us * 1e-6) / 1e12, 1)}),
+                  flush=True)
+        del graph, A, B, C
     return 0
 
 

@@ -373,6 +373,53 @@ def test_concurrent_host_threads():
         assert_bits_equal(o.cpu().numpy(), ref, f"thread {i}")
 
 
+def test_hip_graph_capture_and_replay():
+    """The library allocates nothing and sets no memory, so its launches can
+    be captured in a HIP graph: one capture of a GEMM per block tile, K = 0
+    included, replayed several times with eager work and synchronisations in
+    between; every replay must match the oracle bit for bit."""
+    _announce("graph")
+    rng = np.random.default_rng(41)
+    m, n, k = 300, 270, 200
+    a = (rng.integers(-8, 9, size=(m, k)) / 8).astype(np.float16)
+    b = (rng.integers(-8, 9, size=(n, k)) / 8).astype(np.float16)
+    ref = oracle.gemm_f16_nt(a, b)
+    dev = torch.device("cuda")
+    a_d, b_d = torch.from_numpy(a).to(dev), torch.from_numpy(b).to(dev)
+    outs = [torch.empty((m, n), dtype=torch.float16, device=dev) for _ in TILES]
+    zero_out = torch.empty((m, n), dtype=torch.float16, device=dev)
+    # warm the library's per-device caches outside the capture
+    g.gemm_f16_nt(a_d, b_d, out=outs[0])
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()  # default priority
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        with torch.cuda.graph(graph, stream=side):
+            cap = torch.cuda.current_stream()
+            for t, o in zip(TILES, outs):
+                rc = g.gemm_f16_nt_raw(m, n, k, a_d.data_ptr(), b_d.data_ptr(), o.data_ptr(), cap.cuda_stream,
+                                       tile=t)
+                assert rc == g.OK, g.status_string(rc)
+            rc = g.gemm_f16_nt_raw(m, n, 0, a_d.data_ptr(), b_d.data_ptr(), zero_out.data_ptr(), cap.cuda_stream)
+            assert rc == g.OK, g.status_string(rc)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    for rep in range(4):
+        for o in outs:
+            o.view(torch.int16).fill_(SENTINEL)  # eager work between replays
+        zero_out.view(torch.int16).fill_(SENTINEL)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for t, o in zip(TILES, outs):
+            assert_bits_equal(o.cpu().numpy(), ref, f"replay {rep} tile {t}")
+        assert bool((zero_out.view(torch.int16) == 0).all()), f"replay {rep}: K = 0 output not zero"
+        # eager calls between replays
+        g.gemm_f16_nt(a_d, b_d, out=outs[0])
+        torch.cuda.synchronize()
+
+
 @pytest.mark.parametrize("a_off,b_off", [(1, 0), (0, 3), (5, 7)])
 def test_unaligned_operands_take_the_scalar_loader(a_off, b_off):
     _announce("unaligned", a_off, b_off)
