@@ -54,16 +54,26 @@ def cpu_baseline(a, b, c_gpu, w, budget_s: float):
 
     threads = oracle.default_threads()
     rng = np.random.default_rng(12345)
-    # calibrate on one row per thread, then size the sample to the time budget
+    # Calibrate on one row per thread, then run random rows in batches of
+    # about a quarter of the budget until the budget is spent.  The small
+    # calibration call also pays for starting threads and cold caches, so
+    # the batches, not the calibration, decide how many rows fit.
     t0 = time.perf_counter()
     first = oracle.gemm_f16_nt_rows(a, b, list(range(min(threads, w.m))), threads)
     t_round = max(time.perf_counter() - t0, 1e-6)  # one row on every thread
-    rows_fit = int(budget_s / t_round) * threads
-    nrows = max(threads, min(w.m, (rows_fit // threads) * threads or threads))
-    rows = np.sort(rng.choice(w.m, size=min(nrows, w.m), replace=False))
-    t0 = time.perf_counter()
-    ref = oracle.gemm_f16_nt_rows(a, b, rows, threads)
-    dt = time.perf_counter() - t0
+    batch = max(threads, int(budget_s / 4.0 / t_round) * threads)
+    order = rng.permutation(w.m)
+    row_parts, ref_parts = [], []
+    dt, done = 0.0, 0
+    while done < w.m and (dt < budget_s or done == 0):
+        rows_b = np.sort(order[done:done + batch])
+        t0 = time.perf_counter()
+        ref_parts.append(oracle.gemm_f16_nt_rows(a, b, rows_b, threads))
+        dt += time.perf_counter() - t0
+        row_parts.append(rows_b)
+        done += len(rows_b)
+    rows = np.concatenate(row_parts)
+    ref = np.concatenate(ref_parts)
     flops = 2.0 * len(rows) * w.n * w.k
     rec = {
         "value": round(flops / dt / 1e12, 6),
