@@ -35,6 +35,9 @@ def main(argv=None) -> int:
     ap.add_argument("--ceiling", action="store_true",
                     help="instead: the sustained v_mfma_f32_32x32x16_f16 and v_mfma_f32_16x16x32_f16 rates of the device with no "
                          "global memory traffic (libmfma_ceiling.so), on random and on zero operands")
+    ap.add_argument("--hold", type=float, default=0.0, metavar="SECONDS",
+                    help="with --data: run each operand set back to back for this long and print its "
+                         "wall-clock start and end (to line up with power and clock samples)")
     ap.add_argument("--graph", type=int, default=0, metavar="N",
                     help="instead: time N GEMMs of each shape (default 256^3, 1024^3, 2048^3) launched "
                          "eagerly and replayed from one captured HIP graph")
@@ -106,6 +109,8 @@ def data_sweep(a, torch) -> int:
     C = torch.empty((m, n), device="cuda", dtype=torch.float16)
     stream = torch.cuda.current_stream()
     data = {name: (f((m, k)), f((n, k))) for name, f in makers.items()}
+    if a.hold > 0:
+        return hold_sweep(a, torch, m, n, k, data, C, stream)
     times = {name: [] for name in data}
     for _ in range(a.rounds):
         for name, (A, B) in data.items():
@@ -127,6 +132,34 @@ def data_sweep(a, torch) -> int:
         us = statistics.median(t) * 1e3
         print(json.dumps({"shape": [m, n, k], "operands": name, "us": round(us, 1),
                           "tflops": round(2.0 * m * n * k / (us * 1e-6) / 1e12, 1)}), flush=True)
+    return 0
+
+
+def hold_sweep(a, torch, m, n, k, data, C, stream) -> int:
+    """Each operand set back to back for a.hold seconds, synchronising every
+    50 launches; one JSON line per set with its wall-clock interval."""
+    import time
+
+    for name, (A, B) in data.items():
+        def run():
+            rc = g.gemm_f16_nt_raw(m, n, k, A.data_ptr(), B.data_ptr(), C.data_ptr(), stream.cuda_stream)
+            if rc != g.OK:
+                raise g.GemmError(rc)
+        for _ in range(5):
+            run()
+        torch.cuda.synchronize()
+        t0 = time.time()
+        launches = 0
+        while time.time() - t0 < a.hold:
+            for _ in range(50):
+                run()
+            torch.cuda.synchronize()
+            launches += 50
+        t1 = time.time()
+        print(json.dumps({"shape": [m, n, k], "operands": name, "start": round(t0, 3), "end": round(t1, 3),
+                          "launches": launches,
+                          "tflops": round(2.0 * m * n * k * launches / (t1 - t0) / 1e12, 1)}), flush=True)
+        time.sleep(1.0)  # an idle gap between sets in the samples
     return 0
 
 
