@@ -193,7 +193,7 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "f16 (fp32 accumulate)",
+        "dtype": "f16",  # fp16 operands; the accumulation (fp32) is named in the metric
         "data": "synthetic",
         "config": {"workload": w.name, "m": w.m, "n": w.n, "k": w.k, "values": w.dist,
                    "tile": args.tile or g.select_tile(w.m, w.n, w.k)},
@@ -211,7 +211,7 @@ def main() -> int:
     }
     if nn:
         rec["metric"] = "fp16 GEMM D = A*B (B [K,N], fp32 out) TFLOP/s; % of MI355X dense fp16 MFMA peak"
-        rec["dtype"] = "f16 in, fp32 accumulate and out"
+        rec["dtype"] = "f16"
     if args.cpu_budget > 0 and not nn:
         print("[bench] CPU baseline (oracle on sampled rows)", file=sys.stderr, flush=True)
         c_host = c.cpu().numpy()
