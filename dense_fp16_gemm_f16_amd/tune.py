@@ -36,8 +36,9 @@ def main(argv=None) -> int:
                     help="instead: the sustained v_mfma_f32_32x32x16_f16 and v_mfma_f32_16x16x32_f16 rates of the device with no "
                          "global memory traffic (libmfma_ceiling.so), on random and on zero operands")
     ap.add_argument("--hold", type=float, default=0.0, metavar="SECONDS",
-                    help="with --data: run each operand set back to back for this long and print its "
-                         "wall-clock start and end (to line up with power and clock samples)")
+                    help="with --data or --ceiling: run each operand set (or probe variant) back to back "
+                         "for this long and print its wall-clock start and end (to line up with power and "
+                         "clock samples)")
     ap.add_argument("--graph", type=int, default=0, metavar="N",
                     help="instead: time N GEMMs of each shape (default 256^3, 1024^3, 2048^3) launched "
                          "eagerly and replayed from one captured HIP graph")
@@ -249,6 +250,25 @@ def ceiling(a, torch) -> int:
                 if rc != 0:
                     raise RuntimeError(f"mfma_ceiling_launch returned {rc}")
             run(iters // 20)
+            if a.hold > 0:
+                # back to back for a.hold seconds, with the wall-clock interval
+                # printed (to line up with power and clock samples)
+                import time
+
+                torch.cuda.synchronize()
+                t0 = time.time()
+                launches = 0
+                while time.time() - t0 < a.hold:
+                    run(iters)
+                    torch.cuda.synchronize()
+                    launches += 1
+                t1 = time.time()
+                tf = L.mfma_ceiling_flops(iters, wgs) * launches / (t1 - t0) / 1e12
+                print(json.dumps({"probe": probes[variant] + ", 128x128 wave tile", "variant": names[variant],
+                                  "operands": operands, "start": round(t0, 3), "end": round(t1, 3),
+                                  "launches": launches, "tflops": round(tf, 1)}), flush=True)
+                time.sleep(1.0)
+                continue
             ms = []
             for _ in range(max(a.rounds, 3)):
                 e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
