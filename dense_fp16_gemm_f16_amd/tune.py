@@ -224,9 +224,12 @@ def ceiling(a, torch) -> int:
     import ctypes
     import os
 
-    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmfma_ceiling.so")
+    from dense_fp16_gemm_f16_amd import build
+
+    path = build.CEILING_LIB
     if not os.path.exists(path):
-        raise RuntimeError(f"{path} is not built: run dense_fp16_gemm_f16_amd.build")
+        raise RuntimeError(f"{path} is not built: run dense_fp16_gemm_f16_amd.build.build_ceiling() "
+                           "(a measurement probe, not part of the library)")
     L = ctypes.CDLL(path)
     L.mfma_ceiling_launch.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p,
                                       ctypes.c_void_p, ctypes.c_void_p]

@@ -167,7 +167,7 @@ static int run(int64_t m, int64_t n, int64_t k, const uint16_t *a,
                           table};
         if (t == nthreads - 1) {
             run_rows(&jobs[t]);
-        } else if (pthread_create(&tid[t], NULL, run_rows, &jobs[t]) == 0) {
+        } else if (pthread_create(&tid[started], NULL, run_rows, &jobs[t]) == 0) {
             ++started;
         } else {
             run_rows(&jobs[t]);
@@ -268,7 +268,7 @@ int oracle_gemm_f16_nn_f64(int64_t m, int64_t n, int64_t k, const uint16_t *a,
                              nrows * t / nthreads, nrows * (t + 1) / nthreads, table};
         if (t == nthreads - 1) {
             run_rows_nn(&jobs[t]);
-        } else if (pthread_create(&tid[t], NULL, run_rows_nn, &jobs[t]) == 0) {
+        } else if (pthread_create(&tid[started], NULL, run_rows_nn, &jobs[t]) == 0) {
             ++started;
         } else {
             run_rows_nn(&jobs[t]);

@@ -3,9 +3,10 @@ host logic (argument checks, status strings, tile scheduler, tile choice)
 behaves as documented.  No GPU is needed: every call here returns before the
 library makes its first HIP call.
 """
-import ctypes
 import os
 import re
+import subprocess
+import sys
 
 import pytest
 
@@ -28,28 +29,6 @@ def test_library_exports_every_declared_symbol():
     L = g.lib()
     for name in declared:
         assert hasattr(L, name), name
-
-
-def test_ceiling_probe_exports_its_header():
-    """libmfma_ceiling.so (the MFMA-rate probe) exports what its header declares."""
-    hdr = open(os.path.join(ROOT, "include", "mfma_ceiling.h")).read()
-    hdr = re.sub(r"/\*.*?\*/", "", hdr, flags=re.S)
-    declared = sorted(set(re.findall(r"\b(mfma_ceiling_\w+)\s*\(", hdr)))
-    assert declared == ["mfma_ceiling_flops", "mfma_ceiling_launch"]
-    L = ctypes.CDLL(os.path.join(ROOT, "dense_fp16_gemm_f16_amd", "libmfma_ceiling.so"))
-    for name in declared:
-        assert hasattr(L, name), name
-    L.mfma_ceiling_launch.argtypes = [ctypes.c_int, ctypes.c_int64, ctypes.c_int32, ctypes.c_void_p,
-                                      ctypes.c_void_p, ctypes.c_void_p]
-    L.mfma_ceiling_flops.argtypes = [ctypes.c_int64, ctypes.c_int32]
-    L.mfma_ceiling_flops.restype = ctypes.c_double
-    # argument checks return before any HIP call
-    assert L.mfma_ceiling_launch(4, 1, 1, 16, 16, None) == -1
-    assert L.mfma_ceiling_launch(-1, 1, 1, 16, 16, None) == -1
-    assert L.mfma_ceiling_launch(0, 0, 1, 16, 16, None) == -1
-    assert L.mfma_ceiling_launch(0, 1, 1, None, 16, None) == -2
-    assert L.mfma_ceiling_launch(0, 1, 1, 8, 16, None) == -3
-    assert L.mfma_ceiling_flops(10, 256) == 10 * 2 * 16 * 32768 * 4 * 256
 
 
 def test_status_strings():
@@ -149,3 +128,32 @@ def test_nn_argument_checks(args, expect):
 
 def test_nn_rejects_the_16x16_tile():
     assert g.gemm_f16_nn_f32_raw(8, 8, 8, FAKE_A, FAKE_B, FAKE_C, 0, g.TILE_128x128_M16) == g.EINVAL
+
+
+# The device gate: GEMM_F16_TEST_ARCH, read when the library loads, stands in
+# for the device's architecture name, so the refusal runs on any host.  Only
+# names that must be refused are tried: an accepted one would go on to launch.
+@pytest.mark.parametrize("arch", ["gfx942", "gfx90a", "gfx9500", "gfx95", "gfx951", "", "gfx1100"])
+def test_device_gate_refuses_other_architectures(arch):
+    code = (
+        "import dense_fp16_gemm_f16_amd as g\n"
+        f"A, B, C = {FAKE_A}, {FAKE_B}, {FAKE_C}\n"
+        "print(g.lib().gemm_f16_nt(4, 4, 4, A, B, C, None), g.lib().gemm_f16_nn_f32(4, 4, 4, A, B, C, None),"
+        " g.lib().gemm_f16_nt(4, 4, 0, A, B, C, None), g.status_string(g.EDEVICE))\n"
+    )
+    env = dict(os.environ, GEMM_F16_TEST_ARCH=arch, PYTHONPATH=ROOT)
+    out = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True, check=True)
+    nt, nn, k0, msg = out.stdout.split(maxsplit=3)
+    assert (int(nt), int(nn), int(k0)) == (g.EDEVICE, g.EDEVICE, g.EDEVICE)
+    assert "gfx950" in msg
+
+
+def test_argument_errors_come_before_the_device_gate():
+    code = (
+        "import dense_fp16_gemm_f16_amd as g\n"
+        f"print(g.lib().gemm_f16_nt(-1, 4, 4, {FAKE_A}, {FAKE_B}, {FAKE_C}, None),"
+        f" g.lib().gemm_f16_nt(0, 4, 4, {FAKE_A}, {FAKE_B}, {FAKE_C}, None))\n"
+    )
+    env = dict(os.environ, GEMM_F16_TEST_ARCH="gfx942", PYTHONPATH=ROOT)
+    out = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True, check=True)
+    assert [int(x) for x in out.stdout.split()] == [g.EINVAL, g.OK]

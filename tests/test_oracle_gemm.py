@@ -7,6 +7,8 @@ exact rational sums on tiny shapes, closed forms that follow from C = A * B^T
 {-8..8}/8 inputs of "wgmma_gemm.cu" (day 78), where every partial sum is a
 multiple of 1/64 and no summation order can round.
 """
+import os
+
 import numpy as np
 import pytest
 
@@ -170,3 +172,36 @@ def test_no_double_rounding_via_fp32():
     a = np.array([[1.0, 2.0**-11, 2.0**-15]], dtype=np.float16)
     b = np.array([[1.0, 1.0, 2.0**-15]], dtype=np.float16)
     assert oracle.gemm_f16_nt(a, b).view(np.uint16)[0, 0] == 0x3C01
+
+
+def test_threads_that_cannot_start_run_inline():
+    """With the address space capped, most of 64 requested threads cannot get
+    a stack: their row ranges run on the calling thread instead, the threads
+    that did start are joined, and C is the same as with one thread."""
+    import subprocess
+    import sys
+    import textwrap
+
+    code = textwrap.dedent("""
+        import resource, sys
+        import numpy as np
+        import oracle
+        rng = np.random.default_rng(5)
+        a = (rng.integers(-8, 9, (192, 40)) / 8).astype(np.float16)
+        b = (rng.integers(-8, 9, (24, 40)) / 8).astype(np.float16)
+        one = oracle.gemm_f16_nt(a, b, nthreads=1)
+        one_nn = oracle.gemm_f16_nn_f64(a, np.ascontiguousarray(b.T), nthreads=1)
+        vm = [int(l.split()[1]) for l in open('/proc/self/status') if l.startswith('VmSize')][0] * 1024
+        cap = vm + 40 * 2**20   # room for a few 8 MiB thread stacks, not 63
+        resource.setrlimit(resource.RLIMIT_AS, (cap, cap))
+        many = oracle.gemm_f16_nt(a, b, nthreads=64)
+        many_nn = oracle.gemm_f16_nn_f64(a, np.ascontiguousarray(b.T), nthreads=64)
+        ok = np.array_equal(one.view(np.uint16), many.view(np.uint16))
+        ok = ok and all(np.array_equal(x, y) for x, y in zip(one_nn, many_nn))
+        print("ok" if ok else "mismatch")
+    """)
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    env = dict(os.environ, PYTHONPATH=root)
+    out = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True, timeout=120)
+    assert out.returncode == 0, out.stderr[-2000:]
+    assert out.stdout.strip() == "ok"
