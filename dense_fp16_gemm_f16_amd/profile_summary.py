@@ -28,8 +28,12 @@ CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
 
 
 def kernel_source_hash() -> str:
+    """Hash of every source the library's kernels are built from (the host
+    side, the kernel templates, the scheduler and the per-tile units)."""
     h = hashlib.sha256()
-    for name in ("gemm_f16.hip", "tile_sched.h"):
+    names = ["gemm_f16.hip", "kernels.h", "tile_sched.h"] + sorted(
+        os.path.basename(p) for p in glob.glob(os.path.join(CSRC, "tile_*.hip")))
+    for name in names:
         with open(os.path.join(CSRC, name), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
