@@ -134,6 +134,20 @@ constexpr uint32_t kOutOfRange = 0x80000000u;  // buffer offset past any num_rec
 #ifndef GEMM_PERSIST
 #define GEMM_PERSIST 1
 #endif
+// 1: C = A B^T's one-workgroup-per-CU kernel stores each tile's C under the
+// MFMAs around the tile change (gemm_f16_stream_kernel)
+#ifndef GEMM_STREAM
+#define GEMM_STREAM 1
+#endif
+// 1: the stream kernel's store units run p (column pair) fastest
+#ifndef GEMM_UNIT_P_FAST
+#define GEMM_UNIT_P_FAST 1
+#endif
+// 1: the stream kernel's stores carry the streaming hint where C's rows are
+// whole 128-byte lines
+#ifndef GEMM_STREAM_NT
+#define GEMM_STREAM_NT 1
+#endif
 // sixteenths of a K-tile's loads issued in step 0 (the rest in step 1)
 #ifndef GEMM_AHEAD_STEP0_LOADS
 #define GEMM_AHEAD_STEP0_LOADS 10
@@ -831,22 +845,30 @@ __device__ __forceinline__ void vm_barrier() {
 
 // Operand stored [rows, K] row-major, K % 64 == 0.  LDS stage: ROWS rows of
 // 128 bytes (the K-tile's 64 fp16); the 16-byte chunk c (k 8c..8c+7) of row
-// r sits at slot c ^ ((r >> 1) & 7).  A load instruction of one wave fills a
-// 1 KB block = 8 rows: lane l writes slot l % 8 of row l / 8 and so fetches
-// the chunk that belongs there; the 8 lanes of a row still read one 128-byte
-// segment.  A fragment read puts 16 consecutive rows at one chunk on every
-// 16 lanes; two rows fill a 256-byte bank window and the swizzle gives the
-// 8 rows of each parity 8 distinct slots, so ds_read_b128 has no conflicts.
-// Fragments: 32x32x16 lane l takes row l % 32, chunk 2 ks + l / 32 (k step
-// ks of 16); 16x16x32 lane l takes row l % 16, chunk 4 ks + l / 16 (k step
-// ks of 32).
+// r sits at slot c ^ sw(r).  A load instruction of one wave fills a 1 KB
+// block = 8 rows: lane l writes slot l % 8 of row l / 8 and so fetches the
+// chunk that belongs there; the 8 lanes of a row still read one 128-byte
+// segment.  A fragment read puts 16 rows at one chunk on every 16 lanes; two
+// rows fill a 256-byte bank window, so the read is free of bank conflicts
+// when those 16 rows take 16 distinct (row parity, slot) pairs.
+//  * PERM false: fragment f, lane l reads row 16 f + l % 16 (consecutive
+//    rows; 32x32x16: row 32 f + l % 32), and sw(r) = (r >> 1) & 7.
+//  * PERM true (16x16x32 only): within each pair of fragments (2p, 2p + 1)
+//    the rows are interleaved by fours: fragment 2p + s, lane l reads row
+//    32 p + 8 ((l % 16) / 4) + 4 s + l % 4, and sw(r) = ((r >> 1) & 1) |
+//    ((r >> 3) & 3) << 1.  As the MFMA's first operand this puts 8
+//    consecutive rows (n of C) of one output row in a lane's two result
+//    blocks 2p and 2p + 1, so C leaves in 16-byte stores straight from the
+//    accumulators.
+// Fragments: 32x32x16 lane l takes chunk 2 ks + l / 32 (k step ks of 16);
+// 16x16x32 lane l takes chunk 4 ks + l / 16 (k step ks of 32).
 // KFULL: K % 64 == 0.  Otherwise (K % 8 == 0) the lanes whose chunk lies
 // past K get an out-of-range offset; an out-of-range lane of a direct load
 // writes zeros into LDS (measured on gfx950), so the partial last K-tile
 // reads as zero-padded.  A lane's chunk index is the same in every load of
 // every K-tile (the swizzle's row bits do not change between a wave's
 // blocks), so the mask is one compare per K-tile.
-template <class C, int ROWS, bool KFULL = true>
+template <class C, int ROWS, bool KFULL = true, bool PERM = false>
 struct KMajorDirect {
     static constexpr int kRow = 128;
     static constexpr int kStage = ROWS * kRow;
@@ -855,14 +877,21 @@ struct KMajorDirect {
     static constexpr int kLoads = kBlocks / C::kWaves;  // per wave and K-tile
     static_assert(C::BK == 64, "a 64-wide K-tile: 8 chunks per row");
     static_assert(kBlocks % C::kWaves == 0, "whole blocks per wave");
-    static_assert(C::kWaves % 2 == 0, "a lane's chunk index is the same in all its loads");
+    // rows of a wave's loads differ by multiples of 8 kWaves, which must
+    // leave the swizzle's row bits (1-3, or 1, 3 and 4) alone
+    static_assert(C::kWaves % (PERM ? 4 : 2) == 0, "a lane's chunk index is the same in all its loads");
+    static_assert(!PERM || C::MB == 16, "interleaved fragment rows serve 16x16x32 tiles");
+
+    static __device__ __forceinline__ int sw(int r) {
+        return PERM ? (((r >> 1) & 1) | (((r >> 3) & 3) << 1)) : ((r >> 1) & 7);
+    }
 
     uint32_t voff[kLoads];
     __amdgpu_buffer_rsrc_t rsrc0, rsrc_none;
     int k_tiles;
     int k_elems, kc;  // !KFULL: K, and k of this lane's chunk inside a K-tile
     int lds_w;     // this wave's first block of stage 0
-    int r_lane[C::KS]; // fragment 0 of k step ks in stage 0
+    int r_lane[PERM ? 2 : 1][C::KS]; // fragment 0 (PERM: fragments 0 and 1) of k step ks in stage 0
 
     __device__ __forceinline__ void init(const _Float16 *base, int rows_valid, int K, int kt_count, int wave,
                                          int lane, int frag_row, int lds) {
@@ -873,16 +902,20 @@ struct KMajorDirect {
 #pragma unroll
         for (int i = 0; i < kLoads; ++i) {
             const int row = (i * C::kWaves + wave) * 8 + (lane >> 3);
-            const int c = (lane & 7) ^ ((row >> 1) & 7);
+            const int c = (lane & 7) ^ sw(row);
             voff[i] = (uint32_t)(row * K + c * 8) * 2u;
             if (i == 0) kc = c * 8;
         }
         lds_w = lds + wave * 1024;
-        const int frow = frag_row + lane % C::MB, q = lane / C::MB, sw = (frow >> 1) & 7;
+        const int q = lane / C::MB, l16 = lane % C::MB;
         constexpr int kChunksPerStep = C::MK / 8;
 #pragma unroll
-        for (int ks = 0; ks < C::KS; ++ks)
-            r_lane[ks] = lds + frow * kRow + (((kChunksPerStep * ks + q) ^ sw) << 4);
+        for (int s = 0; s < (PERM ? 2 : 1); ++s) {
+            const int frow = frag_row + (PERM ? 8 * (l16 >> 2) + 4 * s + (l16 & 3) : l16);
+#pragma unroll
+            for (int ks = 0; ks < C::KS; ++ks)
+                r_lane[s][ks] = lds + frow * kRow + (((kChunksPerStep * ks + q) ^ sw(frow)) << 4);
+        }
     }
 
     // load i of K-tile t into stage S; past K an empty range (reads 0)
@@ -914,7 +947,10 @@ struct KMajorDirect {
     }
 
     __device__ __forceinline__ half8 read(const char *smem, int stage, int ks, int f) const {
-        return *reinterpret_cast<const half8 *>(smem + r_lane[ks] + stage * kStage + f * C::MB * kRow);
+        if constexpr (PERM)
+            return *reinterpret_cast<const half8 *>(smem + r_lane[f & 1][ks] + stage * kStage + (f >> 1) * 32 * kRow);
+        else
+            return *reinterpret_cast<const half8 *>(smem + r_lane[0][ks] + stage * kStage + f * C::MB * kRow);
     }
 };
 
@@ -1711,6 +1747,310 @@ void gemm_f16_persistent_kernel(const Params p) {
     __builtin_amdgcn_s_waitcnt(0);
 }
 
+// v_mfma_f32_16x16x32_f16 with srcC = 0: the first MFMA of an accumulator
+// block in a tile overwrites it.  The accumulator stays tied ("+a") so its
+// registers do not move; the instruction does not read it.
+__device__ __forceinline__ void mfma16_first(half8 a, half8 b, floatx4 &c) {
+    asm volatile("v_mfma_f32_16x16x32_f16 %0, %1, %2, 0" : "+a"(c) : "v"(a), "v"(b));
+}
+
+// C = A B^T with one workgroup per CU walking tiles (blockIdx.x, + gridDim.x,
+// ...), like gemm_f16_persistent_kernel and under the same conditions, but
+// with each tile's C leaving under the MFMAs around the tile change instead
+// of in a pause between tiles.
+//
+// B's fragment rows are interleaved (KMajorDirect PERM), so a lane's result
+// blocks (2p, i) and (2p + 1, i) hold 8 consecutive n of one row m of C:
+// "unit" u = p FM + i, one 16-byte store.  The last K-tile of a tile reads
+// the next tile's first fragments like any other, so the K-tile stream runs
+// on unbroken; step 0 of a tile's first K-tile runs its MFMAs in unit order
+// (blocks (2p, i), (2p + 1, i) back to back) with srcC = 0, and right before
+// the MFMA that overwrites unit u (its MFMA 2u) the previous tile's unit u
+// is read from the accumulators, rounded to fp16 (nearest even) and
+// stored: one store every two MFMAs, each at least NM - 1 MFMAs after the
+// unit's last MFMA (far more than the MFMA result latency).  Stores and
+// loads share the in-order vmcnt counter, so the step-1 acquire barrier of
+// that K-tile leaves the U stores in flight and the next K-tile's waits for
+// them.  The last tile stores its units after the loop.  NT: the stores carry the
+// streaming (non-temporal) hint, for C whose rows are whole 128-byte lines:
+// the C lines then do not displace the A and B lines that other workgroups
+// of the XCD still read from L2 (rows that end inside a line were measured
+// slower with the hint).  The host decides, so no store is behind a branch.
+template <class C, bool NT>
+__global__ __launch_bounds__(C::kThreads)
+__attribute__((amdgpu_waves_per_eu(C::kMinWavesPerEU, C::kMinWavesPerEU)))
+void gemm_f16_stream_kernel(const Params p) {
+    constexpr int BM = C::BM, BN = C::BN;
+    constexpr int TM = C::TM, TN = C::TN, FM = C::FM, FN = C::FN;
+    static_assert(C::MB == 16 && C::KS == 2, "two 32-wide k steps per K-tile");
+    static_assert(FN % 2 == 0, "B fragments in pairs");
+    using OpA = KMajorDirect<C, BM, true>;
+    using OpB = KMajorDirect<C, BN, true, true>;
+    constexpr int kLdsB = OpA::kLdsBytes;
+    constexpr int kLds = OpA::kLdsBytes + OpB::kLdsBytes;
+    constexpr int LA = OpA::kLoads, L = OpA::kLoads + OpB::kLoads;
+    constexpr int NM = FM * FN;  // MFMAs per k step
+    constexpr int U = NM / 2;    // 16-byte store units per wave and tile
+    static_assert(NM >= 16, "the store units need a window of several MFMAs");
+    static_assert(kLds <= 160 * 1024, "LDS budget");
+    static_assert(OpA::kStage + (FM - 1) * C::MB * 128 < 65536 && OpB::kStage + (FN / 2 - 1) * 32 * 128 < 65536,
+                  "LDS immediates must fit the 16-bit offset field");
+    __shared__ __attribute__((aligned(1024))) char smem[kLds];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const int wm = wave / C::WN;
+    const int wn = wave % C::WN;
+
+    const int kt_count = p.k_tiles;  // even, >= 4 (the host's condition)
+    const int ntiles = p.num_m * p.num_n;
+    const int G = gridDim.x;
+    int idx = blockIdx.x;
+
+    // first rows of A, B and C of a tile and the bytes of its rows inside
+    // the matrices (0 past the last tile: loads read zeros)
+    struct TileRows {
+        const _Float16 *a, *b;
+        _Float16 *c;
+        uint32_t a_bytes, b_bytes, c_bytes;
+        int n0;
+    };
+    auto tile_rows = [&](int id) {
+        TileRows r;
+        if (id < ntiles) {
+            const TileCoord tc = tile_coord(id, p.num_m, p.num_n, p.swizzle, p.xcd != 0);
+            const int m0 = (int)tc.m_block * BM;
+            r.n0 = (int)tc.n_block * BN;
+            const uint32_t rows_a = (uint32_t)min(BM, p.m - m0), rows_b = (uint32_t)min(BN, p.n - r.n0);
+            r.a = p.a + (int64_t)m0 * p.k;
+            r.b = p.b + (int64_t)r.n0 * p.k;
+            r.c = static_cast<_Float16 *>(p.c) + (int64_t)m0 * p.n;
+            r.a_bytes = rows_a * (uint32_t)p.k * 2u;
+            r.b_bytes = rows_b * (uint32_t)p.k * 2u;
+            r.c_bytes = rows_a * (uint32_t)p.n * 2u;
+        } else {
+            r.a = p.a;
+            r.b = p.b;
+            r.c = static_cast<_Float16 *>(p.c);
+            r.a_bytes = r.b_bytes = r.c_bytes = 0u;
+            r.n0 = 0;
+        }
+        // wave-uniform by construction; readfirstlane keeps them in scalar
+        // registers through the K loop
+        auto u32 = [](uint32_t v) { return (uint32_t)__builtin_amdgcn_readfirstlane(v); };
+        auto uptr = [&](auto *q) {
+            const uint64_t v = (uint64_t)(uintptr_t)q;
+            return (decltype(q))(uintptr_t)(((uint64_t)u32((uint32_t)(v >> 32)) << 32) | u32((uint32_t)v));
+        };
+        r.a = uptr(r.a);
+        r.b = uptr(r.b);
+        r.c = uptr(r.c);
+        r.a_bytes = u32(r.a_bytes);
+        r.b_bytes = u32(r.b_bytes);
+        r.c_bytes = u32(r.c_bytes);
+        r.n0 = (int)u32((uint32_t)r.n0);
+        return r;
+    };
+    TileRows cur = tile_rows(idx);
+    TileRows nxt = tile_rows(idx + G);
+    TileRows prv = tile_rows(ntiles);  // before the first tile: nothing to store
+
+    OpA opa;
+    OpB opb;
+    opa.init(cur.a, 0, p.k, kt_count, wave, lane, wm * TM, 0);
+    opb.init(cur.b, 0, p.k, kt_count, wave, lane, wn * TN, kLdsB);
+
+    // Every tile's first MFMA on a block takes srcC = 0, so the accumulators
+    // are never cleared: defining them is enough.
+    floatx4 acc[FN][FM];
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int i = 0; i < FM; ++i) asm volatile("" : "=a"(acc[j][i]));
+
+    half8 af[3][FM];
+    half8 bf[3][FN];
+    constexpr int NR = FM + FN;  // fragment reads per k step
+    // in the order the MFMAs consume them: B0, A0..A(FM-1), B1..
+    auto read_frag = [&](int buf, int stage, int ks, int r) {
+        if (r == 0)
+            bf[buf][0] = opb.read(smem, stage, ks, 0);
+        else if (r <= FM)
+            af[buf][r - 1] = opa.read(smem, stage, ks, r - 1);
+        else
+            bf[buf][r - FM] = opb.read(smem, stage, ks, r - FM);
+    };
+    // load i of K-tile u of the stream: K-tile u of this tile, or u -
+    // kt_count of the next
+    auto load = [&](auto s_c, int u, int i) {
+        constexpr int S = decltype(s_c)::value;
+        const bool next = u >= kt_count;
+        const int t = next ? u - kt_count : u;
+        if (i < LA)
+            opa.template load_tile<S>(smem, next ? nxt.a : cur.a, next ? nxt.a_bytes : cur.a_bytes, t, i);
+        else
+            opb.template load_tile<S>(smem, next ? nxt.b : cur.b, next ? nxt.b_bytes : cur.b_bytes, t, i - LA);
+    };
+
+    // Unit u = (p, i): p fastest, so the units that write the two 64-byte
+    // halves of a 128-byte line of C (p = 2c, 2c + 1) go out back to back.
+    constexpr auto unit_p = [](int u) { return GEMM_UNIT_P_FAST ? u % (FN / 2) : u / FM; };
+    constexpr auto unit_i = [](int u) { return GEMM_UNIT_P_FAST ? u / (FN / 2) : u % FM; };
+    // Store unit u of tile t: lane l holds row 16 i + l % 16 of the wave's
+    // rows and n = 32 p + 8 (l / 16) .. + 7 of its columns; the descriptor
+    // starts at the tile's first row of C, so the offset adds the tile's
+    // first column n0.  A chunk past N
+    // (N % 8 == 0: wholly past) gets an out-of-range offset; rows past M lie
+    // beyond the descriptor's range.
+    const int col_l = wn * TN + 8 * (lane >> 4);
+    const uint32_t lane_off = (uint32_t)((wm * TM + (lane & 15)) * p.n + col_l) * 2u;
+    auto store_unit = [&](auto u_c, const TileRows &t, __amdgpu_buffer_rsrc_t rc) {
+        constexpr int u = decltype(u_c)::value;
+        constexpr int pp = unit_p(u), ii = unit_i(u);
+        // redefine the unit's accumulators here, so their copies to VGPRs
+        // happen here and not all at the top of the step
+        asm volatile("" : "+a"(acc[2 * pp][ii]), "+a"(acc[2 * pp + 1][ii]));
+        half8 v;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            v[e] = (_Float16)acc[2 * pp][ii][e];  // round to nearest even
+            v[4 + e] = (_Float16)acc[2 * pp + 1][ii][e];
+        }
+        // an opaque copy of the lane's offsets: computed here, not hoisted
+        // out of the tile loop as 2 U loop invariants
+        uint32_t lo = lane_off;
+        int cl = col_l;
+        asm volatile("" : "+v"(lo), "+v"(cl));
+        const uint32_t off = (lo + (uint32_t)(16 * ii * p.n + t.n0 + 32 * pp) * 2u) |
+                             (t.n0 + cl + 32 * pp < p.n ? 0u : kOutOfRange);
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(int4v, v), rc, off, 0, NT ? 2 : 0);
+    };
+
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
+    using F = std::false_type;
+    using T = std::true_type;
+    constexpr int kRelAt = GEMM_AHEAD_REL_MFMA < NM ? GEMM_AHEAD_REL_MFMA : NM - 1;
+    constexpr int kAcqAt = GEMM_AHEAD_ACQ_MFMA < NM ? GEMM_AHEAD_ACQ_MFMA : NM - 1;
+    constexpr int L0 = L * GEMM_AHEAD_STEP0_LOADS / 16;  // loads of K-tile t+2 in step 0
+    static_assert(U + L0 < 64, "vmcnt range");
+
+    // Prologue: K-tiles 0 and 1 into stages 0 and 1, both in LDS before the
+    // first K-tile; both steps' fragments of K-tile 0 into buffers 0 and 1.
+#pragma unroll
+    for (int i = 0; i < L; ++i) load(S0{}, 0, i);
+#pragma unroll
+    for (int i = 0; i < L; ++i) load(S1{}, 1, i);
+    vm_barrier<0>();
+#pragma unroll
+    for (int r = 0; r < NR; ++r) read_frag(0, 0, 0, r);
+#pragma unroll
+    for (int r = 0; r < NR; ++r) read_frag(1, 0, 1, r);
+
+    // One K-tile (as gemm_f16_persistent_kernel's).  FIRST: a tile's first
+    // K-tile: step 0 in unit order with srcC = 0, storing the units of the
+    // previous tile (ep, through rc_ep) as it overwrites them.
+    auto k_iter = [&](auto s_c, int t, auto first_c, const TileRows &ep, __amdgpu_buffer_rsrc_t rc_ep) {
+        constexpr int S = decltype(s_c)::value;
+        constexpr bool FIRST = decltype(first_c)::value;
+        constexpr int SN = S ^ 1;
+        opa.refresh_lds();
+        opb.refresh_lds();
+        constexpr int B1 = S == 0 ? 1 : 2;   // this K-tile's step-1 buffer
+        constexpr int NB1 = S == 0 ? 2 : 1;  // the next K-tile's
+        // step 0
+        static_range<0, NM>([&](auto m_c) {
+            constexpr int m = decltype(m_c)::value;
+            if constexpr (FIRST) {
+                constexpr int u = m / 2, j = 2 * unit_p(u) + m % 2, i = unit_i(u);
+                if constexpr (m % 2 == 0) store_unit(std::integral_constant<int, u>{}, ep, rc_ep);
+                mfma16_first(bf[0][j], af[0][i], acc[j][i]);
+            } else {
+                constexpr int j = m / FM, i = (j & 1) ? FM - 1 - m % FM : m % FM;
+                mfma16_tied(bf[0][j], af[0][i], acc[j][i]);
+            }
+            if constexpr (m == kRelAt) lgkm_barrier();
+            if constexpr (m >= kRelAt) {
+                constexpr int q = m - kRelAt, slots = NM - kRelAt;
+                static_range<q * L0 / slots, (q + 1) * L0 / slots>(
+                    [&](auto o_c) { load(s_c, t + 2, decltype(o_c)::value); });
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        });
+#pragma unroll
+        for (int j = 0; j < FN; ++j) asm volatile("" ::"v"(bf[0][j]));
+#pragma unroll
+        for (int i = 0; i < FM; ++i) asm volatile("" ::"v"(af[0][i]));
+        // step 1
+        static_range<0, NM>([&](auto m_c) {
+            constexpr int m = decltype(m_c)::value;
+            constexpr int j = m / FM, i = (j & 1) ? FM - 1 - m % FM : m % FM;
+            mfma16_tied(bf[B1][j], af[B1][i], acc[j][i]);
+            // Acquire: this wave's loads of K-tile t+1 are in LDS; after
+            // them went out the loads of K-tile t+2 of step 0 and, in a
+            // tile's first K-tile, the previous tile's U stores.
+            if constexpr (m == kAcqAt) vm_only_barrier<FIRST ? U + L0 : L0>();
+            if constexpr (m >= kAcqAt) {
+                constexpr int nl = L - L0, total = 2 * NR + nl, slots = NM - kAcqAt, q = m - kAcqAt;
+                // R R L R R L ...: the reads first while both remain
+                static_range<q * total / slots, (q + 1) * total / slots>([&](auto o_c) {
+                    constexpr int o = decltype(o_c)::value;
+                    constexpr int groups = (2 * NR) / 2 < nl ? (2 * NR) / 2 : nl;  // (R, R, L) groups
+                    constexpr bool in_groups = o < 3 * groups;
+                    constexpr bool is_read = in_groups ? (o % 3 != 2) : (2 * NR > 2 * groups);
+                    constexpr int idx2 = in_groups ? (is_read ? (o / 3) * 2 + (o % 3) : o / 3)
+                                                   : (is_read ? 2 * groups + (o - 3 * groups) : groups + (o - 3 * groups));
+                    if constexpr (is_read) {
+                        constexpr int ks = idx2 / NR, r = idx2 % NR;
+                        read_frag(ks == 0 ? 0 : NB1, SN, ks, r);
+                    } else {
+                        load(s_c, t + 2, L0 + idx2);
+                    }
+                });
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        });
+#pragma unroll
+        for (int j = 0; j < FN; ++j) asm volatile("" ::"v"(bf[B1][j]));
+#pragma unroll
+        for (int i = 0; i < FM; ++i) asm volatile("" ::"v"(af[B1][i]));
+    };
+
+    // Every tile runs the same code, with no branch around a K-tile (with
+    // all registers in use, duplicated K-tiles on two paths make the
+    // register allocator spill): the first tile stores the units of a
+    // "previous tile" with an empty range, which are dropped, and the last
+    // reads the fragments of a "next tile" past the grid, zeros.
+    __amdgpu_buffer_rsrc_t rc_prv = make_rsrc(prv.c, 0u);
+    for (;;) {
+        k_iter(S0{}, 0, T{}, prv, rc_prv);
+        k_iter(S1{}, 1, F{}, prv, rc_prv);
+        for (int kt = 2; kt < kt_count; kt += 2) {
+            k_iter(S0{}, kt, F{}, prv, rc_prv);
+            k_iter(S1{}, kt + 1, F{}, prv, rc_prv);
+        }
+        if (idx + G >= ntiles) break;
+        prv = cur;
+        rc_prv = make_rsrc(cur.c, cur.c_bytes);
+        cur = nxt;
+        idx += G;
+        nxt = tile_rows(idx + G);
+    }
+    // the last tile's units
+    acc_fence(acc);
+    {
+        const __amdgpu_buffer_rsrc_t rc = make_rsrc(cur.c, cur.c_bytes);
+        static_range<0, U>([&](auto u_c) {
+            store_unit(u_c, cur, rc);
+            __builtin_amdgcn_sched_barrier(0);
+        });
+    }
+    // the last tile's loads past the tile (zeros into LDS) and its stores
+    // are done before the workgroup ends
+    __builtin_amdgcn_s_waitcnt(0);
+}
+
 // ---- launch ----------------------------------------------------------------
 
 using Cfg256 = Cfg<256, 256, 2, 2>;   // 4 waves, 128x128 each
@@ -1770,8 +2110,19 @@ hipError_t launch(const Params &p, int g, int cus, hipStream_t stream) {
                 // more tiles than CUs: one workgroup per CU walking several
                 // tiles, where its conditions hold
                 if (GEMM_PERSIST && full && p.k_tiles % 2 == 0 && p.k_tiles >= 4 && cus > 0 && tiles > cus &&
-                    p.n % 8 == 0 && ((uintptr_t)p.c % 16) == 0 && (int64_t)CD::BM * p.n * 2 < (int64_t(1) << 31))
-                    return launch_kernel(gemm_f16_persistent_kernel<CD, false>, dim3((unsigned)cus), block, stream, p);
+                    p.n % 8 == 0 && ((uintptr_t)p.c % 16) == 0 && (int64_t)CD::BM * p.n * 2 < (int64_t(1) << 31)) {
+                    if constexpr (GEMM_STREAM && CD::FM * CD::FN >= 16) {
+                        // rows of C that are whole 128-byte lines: streaming stores
+                        const bool lines = GEMM_STREAM_NT && (p.n * 2) % 128 == 0 && ((uintptr_t)p.c % 128) == 0;
+                        return lines ? launch_kernel(gemm_f16_stream_kernel<CD, true>, dim3((unsigned)cus), block,
+                                                     stream, p)
+                                     : launch_kernel(gemm_f16_stream_kernel<CD, false>, dim3((unsigned)cus), block,
+                                                     stream, p);
+                    }
+                    else
+                        return launch_kernel(gemm_f16_persistent_kernel<CD, false>, dim3((unsigned)cus), block, stream,
+                                             p);
+                }
                 return full ? launch_kernel(gemm_f16_direct_ahead_kernel<CD, true, false>, grid, block, stream, p)
                             : launch_kernel(gemm_f16_direct_ahead_kernel<CD, false, false>, grid, block, stream, p);
             } else {

@@ -206,12 +206,15 @@ def test_direct_to_lds_path_bit_exact(m, n, k, tile):
 # More block tiles than CUs, K a multiple of the K-tile with
 # an even count of at least 4, 16-byte aligned C with N % 8 == 0: one
 # workgroup per CU walks several tiles and the K-tile stream runs across the
-# tile changes.  Ragged last tiles in M and N; 1 to 5 tiles per workgroup.
-# N % 64 == 0 (rows of whole 128-byte lines) takes the non-temporal stores.
+# tile changes; on every block tile but 64x64 each tile's C leaves under the
+# next tile's first MFMAs, in 16-byte stores straight from the accumulators.  Ragged last tiles in M and
+# N; 1 to 5 tiles per workgroup; 4 to 10 K-tiles.  N % 64 == 0 (rows of whole
+# 128-byte lines) takes the non-temporal stores.
 PERSISTENT = [(g.TILE_64x64, 1100, 1064, 256), (g.TILE_64x64, 2100, 2104, 256),
               (g.TILE_128x128, 2100, 2088, 384), (g.TILE_256x256, 4200, 4152, 512),
               (g.TILE_256x128, 4200, 2088, 256), (g.TILE_128x256, 2100, 4152, 256),
-              (g.TILE_256x256, 4200, 4096, 512), (g.TILE_128x128, 2100, 2112, 256)]
+              (g.TILE_256x256, 4200, 4096, 512), (g.TILE_128x128, 2100, 2112, 256),
+              (g.TILE_256x256, 8200, 2056, 384), (g.TILE_256x128, 4100, 4104, 640)]
 
 
 @pytest.mark.parametrize("tile,m,n,k", PERSISTENT)
