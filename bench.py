@@ -9,15 +9,19 @@ Timing follows the tutorials' protocol (CUDA-event timed, median of three
 fresh processes, "4. Pipeline Abstraction and Two Consumer Warp Groups",
 section "Performance").  This process never touches the GPU: it draws the
 inputs of every workload once, then starts --procs fresh child processes one
-after another.  Each child, for the headline workload, runs W untimed
-warm-up GEMMs and then exactly K timed GEMMs between two device
-synchronisations, every launch also bracketed by HIP events on the stream it
-runs on (the kernel's average duration, for the roofline figure); then a
-sustained run of back-to-back GEMMs for at least --sustain seconds, and a
-cold-cache figure (a 512 MiB buffer written before each launch).  It then
-times each of the five workloads the same way (50 event-timed launches, 200
-for the launch-bound 256^3).  `value` is the median over the children of the
-headline's K-step wall-clock rate; the per-workload figures are medians too.
+after another.  Each child first times each of the five workloads (5
+warm-up launches, then 50 event-timed ones, 200 for the launch-bound
+256^3), then, for the headline workload, runs W untimed warm-up GEMMs and
+exactly K timed GEMMs between two device synchronisations, every launch
+also bracketed by HIP events on the stream it runs on (the kernel's average
+duration, for the roofline figure); then a sustained run of back-to-back
+GEMMs for at least --sustain seconds, and a cold-cache figure (a 512 MiB
+buffer written before each launch).  `value` is the median over the
+children of the headline's K-step wall-clock rate; the per-workload figures
+are medians too.  The headline thus runs on a device at its operating
+point; the first child also times the headline's first W + K steps on the
+device as it comes from idle ("cold_start"), which on this power-managed
+part run about a tenth slower while the clock ramps.
 
 Afterwards this process times the oracle (plain fp64 triple loop, one fp16
 rounding) on a bounded sample of the headline workload -- whole rows of C --
@@ -142,22 +146,47 @@ def child(args) -> int:
         torch.cuda.synchronize()
         return [s.elapsed_time(e) * 1e3 for s, e in ev]  # us
 
-    # headline: W warm-up steps, then exactly K timed steps between two synchronisations
-    w, bufs, step = setup(args.workload)
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for i in range(args.steps):
-        starts[i].record(stream)
-        step()
-        ends[i].record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    durs = [s.elapsed_time(e) * 1e3 for s, e in zip(starts, ends)]
+    def headline_steps():
+        """W warm-up steps, then exactly K timed steps between two synchronisations."""
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+        ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            starts[i].record(stream)
+            step()
+            ends[i].record(stream)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        return wall, [s.elapsed_time(e) * 1e3 for s, e in zip(starts, ends)]
+
+    # every workload resident first, so no host work idles the device between
+    # the measurements below
+    order = [c for c in CONFIGS if c != args.workload] + [args.workload]
+    setups = {name: setup(name) for name in order}
+    w, bufs, step = setups[args.workload]
+
+    # the first process, before anything else: the headline on a device that
+    # was idle (its clock still ramping), for reference
+    if args.index == 0:
+        wall, durs = headline_steps()
+        out["cold_start"] = {"wall_s": wall, "kernel_us": durs}
+
+    # every workload: 5 warm-up launches, then 50 (256^3: 200) event-timed
+    # ones; the headline workload last
+    for name in order:
+        cw, cbufs, cstep = setups[name]
+        for _ in range(5):
+            cstep()
+        out["configs"][name] = {"kernel_us": event_timed(cstep, 200 if cw.m * cw.n * cw.k < 2**26 else 50),
+                                "tile": args.tile or g.select_tile(cw.m, cw.n, cw.k)}
+    log(f"child {args.index}: five workloads timed")
+
+    # the headline, right after, on a device at its operating point
+    wall, durs = headline_steps()
     out["headline"] = {"workload": w.name, "wall_s": wall, "kernel_us": durs,
                        "tile": args.tile or g.select_tile(w.m, w.n, w.k)}
     log(f"child {args.index}: {w.name} {args.steps} steps, wall/step {wall / args.steps * 1e6:.1f} us, "
@@ -186,23 +215,12 @@ def child(args) -> int:
 
     # outputs for the parity check (first child), from a launch of its own
     if args.index == 0:
-        step()
-        torch.cuda.synchronize()
-        np.save(os.path.join(args.child, f"{w.name}_c.npy"), bufs[2].cpu().numpy())
-    del bufs, step
-
-    # every workload: 5 warm-up launches, then 50 (256^3: 200) event-timed ones
-    for name in CONFIGS:
-        w, bufs, step = setup(name)
-        for _ in range(5):
-            step()
-        out["configs"][name] = {"kernel_us": event_timed(step, 200 if w.m * w.n * w.k < 2**26 else 50),
-                                "tile": args.tile or g.select_tile(w.m, w.n, w.k)}
-        if args.index == 0 and name != args.workload:
-            np.save(os.path.join(args.child, f"{name}_c.npy"), bufs[2].cpu().numpy())
-        del bufs, step
-        torch.cuda.synchronize()
-    log(f"child {args.index}: five workloads timed")
+        for name in order:
+            cw, cbufs, cstep = setups[name]
+            cstep()
+            torch.cuda.synchronize()
+            np.save(os.path.join(args.child, f"{name}_c.npy"), cbufs[2].cpu().numpy())
+    del setups, bufs, step
     with open(os.path.join(args.child, f"result_{args.index}.json"), "w") as f:
         json.dump(out, f)
     return 0
@@ -372,6 +390,12 @@ def main() -> int:
                                 "tflops_per_process": [round(x, 2) for x in rates],
                                 "seconds": round(statistics.median(r["sustained"]["seconds"] for r in results), 3),
                                 "launches": results[0]["sustained"]["launches"]}
+        cs = results[0].get("cold_start")
+        if cs:
+            rec["cold_start"] = {"tflops": round(flops * args.steps / cs["wall_s"] / 1e12, 2),
+                                 "kernel_avg_us": round(statistics.mean(cs["kernel_us"]), 2),
+                                 "what": f"the first process's first {args.warmup} + {args.steps} steps, "
+                                         "on a device that was idle"}
         cold = statistics.median(statistics.median(r["cold_kernel_us"]) for r in results)
         rec["cold_cache"] = {"kernel_median_us": round(cold, 2), "tflops": round(flops / (cold * 1e-6) / 1e12, 2),
                              "flush": "512 MiB written before each launch"}
