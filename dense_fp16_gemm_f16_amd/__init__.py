@@ -32,9 +32,11 @@ TILE_256x256_W8 = 4
 TILE_256x128 = 5
 TILE_128x256 = 6
 TILE_128x128_M16 = 7
+TILE_64x128 = 8
+TILE_128x64 = 9
 TILES = {TILE_256x256: (256, 256), TILE_128x128: (128, 128), TILE_64x64: (64, 64),
          TILE_256x256_W8: (256, 256), TILE_256x128: (256, 128), TILE_128x256: (128, 256),
-         TILE_128x128_M16: (128, 128)}
+         TILE_128x128_M16: (128, 128), TILE_64x128: (64, 128), TILE_128x64: (128, 64)}
 # tiles on v_mfma_f32_16x16x32_f16: the C = A B^T contract only
 M16_TILES = (TILE_128x128_M16,)
 

@@ -34,38 +34,49 @@ static TileShape tile_shape(int tile) {
         case GEMM_F16_TILE_128x256: return {128, 256};
         case GEMM_F16_TILE_128x128: return {128, 128};
         case GEMM_F16_TILE_128x128_M16: return {128, 128};
+        case GEMM_F16_TILE_64x128: return {64, 128};
+        case GEMM_F16_TILE_128x64: return {128, 64};
         default: return {64, 64};
     }
 }
 
 static int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// Automatic block tile: the candidate with the best modelled throughput,
-// (work per launch) / (rounds of one workgroup per CU x per-tile
-// efficiency).  The efficiency factors are relative per-CU throughputs of
-// the tile shapes measured on MI355X (the bigger the tile, the fewer LDS and
-// L2 bytes per flop).  cus: compute units of the device (256 if unknown).
+// Automatic block tile: the candidate with the smallest modelled time
+//     t = c + a * rounds * k_tiles + b * tiles / cus,
+// rounds = ceil(tiles / cus) rounds of one workgroup per CU, k_tiles =
+// ceil(K / 64): a fixed cost per launch (c), the K loop of each round (a per
+// K-tile) and a cost per tile that the one-workgroup-per-CU kernels spread
+// over the CUs (b: prologue, epilogue and C stores).  The coefficients (us)
+// are a least-squares fit, in relative error, to a sweep of every block tile
+// over 42 shapes (M, N from 512 to 16384, K 256 / 1024 / 4096) on MI355X;
+// the model picks a tile within 5% of the fastest on all of them.  Only the
+// ranking matters.  cus: compute units of the device (256 if unknown).  With
+// K % 8 != 0 the 256x256 tile would run as 128x256 (see gemm_impl), so it
+// is not a candidate.
 static int auto_tile(int64_t m, int64_t n, int64_t k, int cus) {
-    (void)k;
     if (cus <= 0) cus = 256;
     struct Cand {
         int id, bm, bn;
-        double eff;
+        double c, a, b;
     };
     static const Cand cands[] = {
-        {GEMM_F16_TILE_256x256, 256, 256, 1.00},
-        {GEMM_F16_TILE_256x128, 256, 128, 0.90},
-        {GEMM_F16_TILE_128x256, 128, 256, 0.90},
-        {GEMM_F16_TILE_128x128, 128, 128, 0.75},
-        {GEMM_F16_TILE_64x64, 64, 64, 0.35},
+        {GEMM_F16_TILE_256x256, 256, 256, 7.58, 1.075, 8.35},
+        {GEMM_F16_TILE_256x128, 256, 128, 5.78, 0.644, 3.73},
+        {GEMM_F16_TILE_128x256, 128, 256, 5.70, 0.645, 3.95},
+        {GEMM_F16_TILE_128x128, 128, 128, 4.53, 0.431, 1.69},
+        {GEMM_F16_TILE_128x64, 128, 64, 3.49, 0.385, 1.02},
+        {GEMM_F16_TILE_64x128, 64, 128, 3.70, 0.387, 0.934},
+        {GEMM_F16_TILE_64x64, 64, 64, 3.35, 0.308, 0.465},
     };
+    const int64_t k_tiles = cdiv(k, 64);
     int best = GEMM_F16_TILE_64x64;
     double best_t = 1e300;
     for (const Cand &c : cands) {
+        if (c.id == GEMM_F16_TILE_256x256 && k % 8 != 0) continue;
         const int64_t tiles = cdiv(m, c.bm) * cdiv(n, c.bn);
         const int64_t rounds = cdiv(tiles, cus);
-        // time ~ rounds * (tile flops) / eff; tile flops ~ bm * bn
-        const double t = (double)rounds * c.bm * c.bn / c.eff;
+        const double t = c.c + c.a * (double)rounds * (double)k_tiles + c.b * (double)tiles / cus;
         if (t < best_t * 0.999) {
             best_t = t;
             best = c.id;
@@ -219,6 +230,8 @@ static int gemm_impl(bool nn, int64_t m, int64_t n, int64_t k, const void *a, co
         case GEMM_F16_TILE_128x256: e = launch_128x256(nn, p, g, cus, s); break;
         case GEMM_F16_TILE_128x128: e = launch_128x128(nn, p, g, cus, s); break;
         case GEMM_F16_TILE_128x128_M16: e = launch_128x128_m16(p, g, cus, s); break;
+        case GEMM_F16_TILE_64x128: e = launch_64x128(nn, p, g, cus, s); break;
+        case GEMM_F16_TILE_128x64: e = launch_128x64(nn, p, g, cus, s); break;
         default: e = launch_64x64(nn, p, g, cus, s); break;
     }
     return e == hipSuccess ? GEMM_F16_OK : GEMM_F16_EHIP;

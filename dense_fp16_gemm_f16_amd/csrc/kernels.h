@@ -2069,6 +2069,10 @@ using Cfg128d = Cfg<128, 128, 2, 2, 16>;
 using Cfg128m16 = Cfg128d;  // v_mfma_f32_16x16x32_f16 on the register-staged path too
 using Cfg64 = Cfg<64, 64, 2, 2>;
 using Cfg64d = Cfg<64, 64, 2, 2, 16>;
+using Cfg64x128 = Cfg<64, 128, 2, 2>;
+using Cfg64x128d = Cfg<64, 128, 2, 2, 16>;
+using Cfg128x64 = Cfg<128, 64, 2, 2>;
+using Cfg128x64d = Cfg<128, 64, 2, 2, 16>;
 
 // One launch of a kernel that takes Params, returning the status of this
 // launch itself (not an error some earlier HIP call left behind).
@@ -2162,5 +2166,7 @@ hipError_t launch_128x256(bool nn, const Params &p, int g, int cus, hipStream_t 
 hipError_t launch_128x128(bool nn, const Params &p, int g, int cus, hipStream_t s);
 hipError_t launch_128x128_m16(const Params &p, int g, int cus, hipStream_t s);
 hipError_t launch_64x64(bool nn, const Params &p, int g, int cus, hipStream_t s);
+hipError_t launch_64x128(bool nn, const Params &p, int g, int cus, hipStream_t s);
+hipError_t launch_128x64(bool nn, const Params &p, int g, int cus, hipStream_t s);
 
 }  // namespace gemm_f16

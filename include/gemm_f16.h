@@ -96,7 +96,9 @@ enum {
     GEMM_F16_TILE_256x128 = 5,     /* 4 waves, each 128x64 of C */
     GEMM_F16_TILE_128x256 = 6,     /* 4 waves, each 64x128 of C */
     GEMM_F16_TILE_128x128_M16 = 7, /* 4 waves, each 64x64 of C, on v_mfma_f32_16x16x32_f16 */
-    GEMM_F16_TILE_LAST = 7
+    GEMM_F16_TILE_64x128 = 8,      /* 4 waves, each 32x64 of C */
+    GEMM_F16_TILE_128x64 = 9,      /* 4 waves, each 64x32 of C */
+    GEMM_F16_TILE_LAST = 9
 };
 
 /* gemm_f16_nt with explicit options; opt == NULL means all defaults. */

@@ -68,7 +68,7 @@ def test_argument_checks_return_before_any_hip_call(args, expect):
     assert g.lib().gemm_f16_nt(*args, None) == expect
 
 
-@pytest.mark.parametrize("opt", [(8, 0, -1), (-1, 0, -1), (0, -1, -1), (0, 0, 2), (0, 0, -2)])
+@pytest.mark.parametrize("opt", [(10, 0, -1), (-1, 0, -1), (0, -1, -1), (0, 0, 2), (0, 0, -2)])
 def test_bad_options_rejected(opt):
     assert g.gemm_f16_nt_raw(8, 8, 8, FAKE_A, FAKE_B, FAKE_C, 0, *opt) == g.EINVAL
 
@@ -99,6 +99,10 @@ def test_select_tile():
     assert g.select_tile(4096, 4096, 4096) == g.TILE_256x256   # 256 tiles: one per CU
     assert g.select_tile(256, 256, 256) == g.TILE_64x64
     assert g.select_tile(5000, 3000, 1000) in g.TILES
+    # short K: the per-tile cost dominates and 128x128 tiles win (measured 13-29%)
+    assert g.select_tile(4096, 4096, 256) == g.TILE_128x128
+    # K % 8 != 0 would run the 256x256 tile as 128x256: never chosen
+    assert g.select_tile(4096, 4096, 4095) != g.TILE_256x256
     with pytest.raises(g.GemmError):
         g.select_tile(-1, 4, 4)
 

@@ -214,7 +214,8 @@ PERSISTENT = [(g.TILE_64x64, 1100, 1064, 256), (g.TILE_64x64, 2100, 2104, 256),
               (g.TILE_128x128, 2100, 2088, 384), (g.TILE_256x256, 4200, 4152, 512),
               (g.TILE_256x128, 4200, 2088, 256), (g.TILE_128x256, 2100, 4152, 256),
               (g.TILE_256x256, 4200, 4096, 512), (g.TILE_128x128, 2100, 2112, 256),
-              (g.TILE_256x256, 8200, 2056, 384), (g.TILE_256x128, 4100, 4104, 640)]
+              (g.TILE_256x256, 8200, 2056, 384), (g.TILE_256x128, 4100, 4104, 640),
+              (g.TILE_64x128, 1100, 2104, 256), (g.TILE_128x64, 2100, 1064, 384)]
 
 
 @pytest.mark.parametrize("tile,m,n,k", PERSISTENT)

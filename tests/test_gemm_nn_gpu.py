@@ -129,7 +129,7 @@ def test_ragged_shapes(m, n, k, tile):
 # chunk, several tiles in both directions.
 NN_DIRECT = [(1, 8, 8), (64, 128, 64), (300, 264, 200), (129, 520, 72), (513, 1032, 520), (257, 392, 1000),
              (70, 136, 8), (1000, 776, 1088)]
-NN_DIRECT_TILES = [t for t in NN_TILES if t != g.TILE_256x256_W8 and t != g.TILE_64x64]
+NN_DIRECT_TILES = [t for t in NN_TILES if t not in (g.TILE_256x256_W8, g.TILE_64x64, g.TILE_128x64)]
 
 
 @pytest.mark.parametrize("m,n,k", NN_DIRECT)
@@ -150,7 +150,8 @@ def test_direct_to_lds_b_path_bit_exact(m, n, k, tile):
 # (fp32 rows of whole 128-byte lines) takes the non-temporal stores.
 NN_PERSISTENT = [(g.TILE_128x128, 2100, 2088, 384), (g.TILE_256x256, 4200, 4152, 512),
                  (g.TILE_256x128, 4200, 2088, 256), (g.TILE_128x256, 2100, 4152, 256),
-                 (g.TILE_256x256, 4200, 4128, 256), (g.TILE_128x256, 2100, 4160, 256)]
+                 (g.TILE_256x256, 4200, 4128, 256), (g.TILE_128x256, 2100, 4160, 256),
+                 (g.TILE_64x128, 1100, 2104, 256)]
 
 
 @pytest.mark.parametrize("tile,m,n,k", NN_PERSISTENT)
