@@ -37,6 +37,10 @@ TILE_128x64 = 9
 TILES = {TILE_256x256: (256, 256), TILE_128x128: (128, 128), TILE_64x64: (64, 64),
          TILE_256x256_W8: (256, 256), TILE_256x128: (256, 128), TILE_128x256: (128, 256),
          TILE_128x128_M16: (128, 128), TILE_64x128: (64, 128), TILE_128x64: (128, 64)}
+# kernel variants (block_k, LDS stages, loader waves) for gemm_f16_nt_ex
+VARIANT_DEFAULT = 0
+VARIANTS = {1: (64, 2, 0), 2: (64, 3, 0), 3: (32, 2, 0), 4: (32, 3, 0), 5: (32, 4, 0),
+            6: (64, 2, 4), 7: (64, 3, 4)}
 # tiles on v_mfma_f32_16x16x32_f16: the C = A B^T contract only
 M16_TILES = (TILE_128x128_M16,)
 
@@ -54,7 +58,7 @@ EXPORTS = (
 
 class Options(ctypes.Structure):
     _fields_ = [("tile", ctypes.c_int32), ("swizzle", ctypes.c_int32),
-                ("xcd", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("xcd", ctypes.c_int32), ("variant", ctypes.c_int32)]
 
 
 class GemmError(RuntimeError):
@@ -101,9 +105,10 @@ def status_string(status: int) -> str:
 
 
 def gemm_f16_nt_raw(m: int, n: int, k: int, a_ptr: int, b_ptr: int, c_ptr: int,
-                    stream: int = 0, tile: int = TILE_AUTO, swizzle: int = 0, xcd: int = -1) -> int:
+                    stream: int = 0, tile: int = TILE_AUTO, swizzle: int = 0, xcd: int = -1,
+                    variant: int = VARIANT_DEFAULT) -> int:
     """Direct call of gemm_f16_nt_ex with integer device pointers; returns the status."""
-    opt = Options(tile, swizzle, xcd, 0)
+    opt = Options(tile, swizzle, xcd, variant)
     return lib().gemm_f16_nt_ex(m, n, k, a_ptr or None, b_ptr or None, c_ptr or None,
                                 stream or None, ctypes.byref(opt))
 

@@ -36,8 +36,10 @@ HIPCC_FLAGS = [
 
 
 def sources() -> list[str]:
-    """Translation units of libgemm_f16.so: the host side and one per block tile."""
-    return [os.path.join(CSRC, "gemm_f16.hip")] + sorted(glob.glob(os.path.join(CSRC, "tile_*.hip")))
+    """Translation units of libgemm_f16.so: the host side, one per block tile and one
+    per block tile of the ring kernel's variants."""
+    return ([os.path.join(CSRC, "gemm_f16.hip")] + sorted(glob.glob(os.path.join(CSRC, "tile_*.hip")))
+            + sorted(glob.glob(os.path.join(CSRC, "ring_*.hip"))))
 
 
 def _hipcc() -> str:

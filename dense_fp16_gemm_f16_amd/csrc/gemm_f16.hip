@@ -85,6 +85,30 @@ static int auto_tile(int64_t m, int64_t n, int64_t k, int cus) {
     return best;
 }
 
+// A kernel variant (options.variant 1..7): block_k and stages of each, and
+// the tiles whose LDS holds its ring (S x (BM + BN) x 2 block_k bytes <= 160
+// KB) and, with loader waves, whose MFMA waves fit in 256 registers (2
+// stages: up to 128x64 per MFMA wave, not 256x256; 3 stages: 128x128
+// only).  The same conditions decide, at compile time, which variants exist
+// (ring_fits in kernels.h).
+static bool variant_ok(bool nn, int tile, int variant, int64_t k, const void *a, const void *b) {
+    static const int bk[] = {0, 64, 64, 32, 32, 32, 64, 64};
+    static const int st[] = {0, 2, 3, 2, 3, 4, 2, 3};
+    if (nn || variant < 1 || variant > GEMM_F16_VARIANT_LAST) return false;
+    if (k <= 0 || k % bk[variant] != 0 || (((uintptr_t)a | (uintptr_t)b) % 16) != 0) return false;
+    int bm, bn;
+    switch (tile) {
+        case GEMM_F16_TILE_256x256: bm = 256, bn = 256; break;
+        case GEMM_F16_TILE_256x128: bm = 256, bn = 128; break;
+        case GEMM_F16_TILE_128x256: bm = 128, bn = 256; break;
+        case GEMM_F16_TILE_128x128: bm = 128, bn = 128; break;
+        default: return false;
+    }
+    const bool prod = variant >= GEMM_F16_VARIANT_PRODUCER_S2;
+    if (prod && bm * bn > (variant == GEMM_F16_VARIANT_PRODUCER_S2 ? 256 * 128 : 128 * 128)) return false;
+    return st[variant] * (bm + bn) * 2 * bk[variant] <= 160 * 1024;
+}
+
 static int check_sizes(int64_t m, int64_t n, int64_t k) {
     if (m < 0 || n < 0 || k < 0) return GEMM_F16_EINVAL;
     // The kernels index rows and columns of C in 32-bit ints, and the last
@@ -161,6 +185,7 @@ static int gemm_impl(bool nn, int64_t m, int64_t n, int64_t k, const void *a, co
     if (opt) o = *opt;
     if (o.tile < 0 || o.tile > GEMM_F16_TILE_LAST || o.swizzle < 0 || o.xcd < -1 || o.xcd > 1)
         return GEMM_F16_EINVAL;
+    if (o.variant != GEMM_F16_VARIANT_DEFAULT && !variant_ok(nn, o.tile, o.variant, k, a, b)) return GEMM_F16_EINVAL;
     if (nn && o.tile == GEMM_F16_TILE_128x128_M16) return GEMM_F16_EINVAL;
     if (m == 0 || n == 0) return GEMM_F16_OK;
     if (!c || (k > 0 && (!a || !b))) return GEMM_F16_ENULL;
@@ -223,6 +248,15 @@ static int gemm_impl(bool nn, int64_t m, int64_t n, int64_t k, const void *a, co
     if ((int64_t)p.num_m * p.num_n >= (int64_t(1) << 31)) return GEMM_F16_EINVAL;
 
     hipError_t e;
+    if (o.variant != GEMM_F16_VARIANT_DEFAULT) {
+        switch (tile) {
+            case GEMM_F16_TILE_256x256: e = launch_ring_256x256(o.variant, p, s); break;
+            case GEMM_F16_TILE_256x128: e = launch_ring_256x128(o.variant, p, s); break;
+            case GEMM_F16_TILE_128x256: e = launch_ring_128x256(o.variant, p, s); break;
+            default: e = launch_ring_128x128(o.variant, p, s); break;
+        }
+        return e == hipSuccess ? GEMM_F16_OK : GEMM_F16_EHIP;
+    }
     switch (tile) {
         case GEMM_F16_TILE_256x256: e = launch_256x256(nn, p, g, cus, s); break;
         case GEMM_F16_TILE_256x256_W8: e = launch_256x256_w8(nn, p, g, cus, s); break;

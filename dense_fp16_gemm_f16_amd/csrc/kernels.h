@@ -2051,6 +2051,246 @@ void gemm_f16_stream_kernel(const Params p) {
     __builtin_amdgcn_s_waitcnt(0);
 }
 
+// ---- configurable ring (the tuning sweep's other axes) -------------------------
+//
+// A one-tile-per-workgroup kernel for C = A B^T whose K-tile width (block_k
+// 32 or 64), LDS ring depth (S stages) and wave roles are template
+// parameters, so the sweep can measure the axes the default kernels fix
+// (block_k 64, 2 stages, every wave loading): the "Pipeline Depth" and
+// producer/consumer ("Two Consumer Warp Groups") variants of "4. Pipeline
+// Abstraction and Two Consumer Warp Groups", on gfx950 terms.  16x16x32 MFMAs
+// with tied accumulators; fragments read one 32-wide k step ahead; one
+// workgroup barrier per K-tile, a few MFMAs into its last k step: before it
+// every wave has finished reading the K-tile's stage and the loading waves
+// have waited for their loads of the next K-tile, so after it the stage is
+// free for the loads of K-tile t + S and the next K-tile is in LDS for
+// everyone.  PROD: 4 more waves that only load (the MFMA waves then issue
+// no global loads); otherwise every wave loads its share, spread over the
+// MFMAs after the barrier.  K % BK == 0; the K-tile count is padded with
+// all-zero K-tiles to a whole number of unrolled blocks (they add +0 to
+// accumulators that are never -0, which leaves every bit as it was).
+
+// Operand stored [rows, K] row-major: LDS stage of ROWS rows of BK fp16
+// (2 BK bytes); the 16-byte chunk c of row r at slot c ^ sw(r).  A fragment
+// read puts 16 consecutive rows at one chunk on 16 lanes, and a 256-byte
+// bank window holds 256 / (2 BK) rows, so the read is free of bank
+// conflicts when those rows take distinct (row mod rows-per-window, slot)
+// pairs: sw(r) = (r >> 1) & 7 for BK 64, (r >> 2) & 3 for BK 32.  A load
+// fills 1 KB: lane l writes slot l % (BK / 8) of row l / (BK / 8) and
+// fetches the chunk that belongs there.  NLW waves load, load i of loading
+// wave w covering rows (i NLW + w) 1024 / (2 BK) ..; those rows differ by
+// multiples of 32, which leaves a lane's slot-to-chunk map the same in all
+// its loads.
+template <class C, int ROWS, int BK, int NLW>
+struct RingOperand {
+    static constexpr int kRow = 2 * BK, kCpr = BK / 8, kRowsPerLoad = 1024 / kRow;
+    static constexpr int kStage = ROWS * kRow;
+    static constexpr int kBlocks = kStage / 1024;
+    static constexpr int kLoads = kBlocks / NLW;  // per loading wave and K-tile
+    static constexpr int KS = BK / 32;            // 32-wide k steps per K-tile
+    static_assert(BK == 32 || BK == 64, "block_k");
+    static_assert(kBlocks % NLW == 0, "whole blocks per loading wave");
+    static_assert((NLW * kRowsPerLoad) % 32 == 0, "a lane's chunk map is the same in all its loads");
+
+    static __device__ __forceinline__ int sw(int r) { return BK == 64 ? ((r >> 1) & 7) : ((r >> 2) & 3); }
+
+    uint32_t voff[kLoads];
+    __amdgpu_buffer_rsrc_t rsrc, rsrc_none;
+    int k_tiles;
+    int lds_w;       // this loading wave's first block of stage 0
+    int r_lane[KS];  // fragment 0 of k step ks, stage 0
+
+    __device__ __forceinline__ void init_loads(const _Float16 *base, int rows_valid, int K, int kt, int lw, int lane,
+                                               int lds) {
+        k_tiles = kt;
+        rsrc = make_rsrc(base, (uint32_t)rows_valid * (uint32_t)K * 2u);
+        rsrc_none = make_rsrc(base, 0u);
+#pragma unroll
+        for (int i = 0; i < kLoads; ++i) {
+            const int row = (i * NLW + lw) * kRowsPerLoad + lane / kCpr;
+            voff[i] = (uint32_t)(row * K + ((lane % kCpr) ^ sw(row)) * 8) * 2u;
+        }
+        lds_w = lds + lw * 1024;
+    }
+
+    __device__ __forceinline__ void init_reads(int frag_row, int lane, int lds) {
+        const int frow = frag_row + lane % 16, q = lane / 16;
+#pragma unroll
+        for (int ks = 0; ks < KS; ++ks) r_lane[ks] = lds + frow * kRow + (((4 * ks + q) ^ sw(frow)) << 4);
+    }
+
+    // load i of K-tile t into stage s (byte offset so); past K an empty range (reads 0)
+    __device__ __forceinline__ void load(char *smem, int so, int t, int i) const {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            t < k_tiles ? rsrc : rsrc_none,
+            (__attribute__((address_space(3))) void *)(smem + lds_w + so + i * NLW * 1024), 16, voff[i],
+            (uint32_t)t * (uint32_t)kRow, 0, 0);
+    }
+
+    __device__ __forceinline__ void refresh_lds() { asm volatile("" : "+s"(lds_w)); }
+
+    __device__ __forceinline__ half8 read(const char *smem, int so, int ks, int f) const {
+        return *reinterpret_cast<const half8 *>(smem + r_lane[ks] + so + f * 16 * kRow);
+    }
+};
+
+template <class C, int BK, int S, bool PROD>
+__global__ __launch_bounds__(C::kThreads *(PROD ? 2 : 1))
+__attribute__((amdgpu_waves_per_eu(PROD ? 2 : C::kMinWavesPerEU, PROD ? 2 : C::kMinWavesPerEU)))
+void gemm_f16_ring_kernel(const Params p) {
+    constexpr int BM = C::BM, BN = C::BN;
+    constexpr int TM = C::TM, TN = C::TN, FM = C::FM, FN = C::FN;
+    constexpr int NC = C::kWaves;        // MFMA waves
+    constexpr int NLW = PROD ? 4 : NC;   // loading waves
+    static_assert(C::MB == 16, "16x16x32 MFMAs");
+    using OpA = RingOperand<C, BM, BK, NLW>;
+    using OpB = RingOperand<C, BN, BK, NLW>;
+    constexpr int KS = OpA::KS;
+    constexpr int kStageAB = OpA::kStage + OpB::kStage;  // one stage: A then B
+    constexpr int kLds = S * kStageAB;
+    constexpr int LA = OpA::kLoads, L = OpA::kLoads + OpB::kLoads;  // per loading wave and K-tile
+    constexpr int NM = FM * FN, NR = FM + FN;
+    // K-tiles per unrolled block: S stages, and an even number of k steps
+    // so that the fragment buffers alternate within it
+    constexpr int kBlk = (S * KS) % 2 == 0 ? S : 2 * S;
+    static_assert(S >= 2 && kLds <= 160 * 1024, "LDS budget");
+    static_assert((S - 1) * L < 64, "vmcnt range");
+    // (a stage offset past the 16-bit LDS immediate costs the compiler an
+    // address add per read; deep rings of large stages pay it)
+    __shared__ __attribute__((aligned(1024))) char smem[kLds];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
+    const bool mfma_wave = !PROD || wave < NC;
+    const int lw = PROD ? wave - NC : wave;  // index among the loading waves
+    const int wm = (wave % NC) / C::WN;
+    const int wn = (wave % NC) % C::WN;
+
+    const TileCoord tc = tile_coord(blockIdx.x, p.num_m, p.num_n, p.swizzle, p.xcd != 0);
+    const int m0 = (int)tc.m_block * BM;
+    const int n0 = (int)tc.n_block * BN;
+    const int kt = p.k / BK;                      // K % BK == 0 (the host's condition)
+    const int tpad = (kt + kBlk - 1) / kBlk * kBlk;  // padded with all-zero K-tiles
+
+    OpA opa;
+    OpB opb;
+    opa.init_loads(p.a + (int64_t)m0 * p.k, min(BM, p.m - m0), p.k, kt, lw, lane, 0);
+    opb.init_loads(p.b + (int64_t)n0 * p.k, min(BN, p.n - n0), p.k, kt, lw, lane, OpA::kStage);
+    opa.init_reads(wm * TM, lane, 0);
+    opb.init_reads(wn * TN, lane, OpA::kStage);
+
+    auto load = [&](int so, int t, int i) {
+        if (i < LA)
+            opa.load(smem, so, t, i);
+        else
+            opb.load(smem, so, t, i - LA);
+    };
+
+    if (PROD && !mfma_wave) {
+        // Loading waves: K-tiles 0 .. S-1 into stages 0 .. S-1; then per
+        // K-tile t, wait for K-tile t + 1 (after it went out K-tiles t + 2
+        // .. t + S - 1), pass the barrier (everyone has read stage t % S)
+        // and load K-tile t + S into it.
+        for (int s = 0; s < S; ++s)
+#pragma unroll
+            for (int i = 0; i < L; ++i) load(s * kStageAB, s, i);
+        vm_barrier<(S - 1) * L>();  // K-tile 0 in LDS: the MFMA waves' first reads
+        for (int t = 0; t < tpad; ++t) {
+            vm_only_barrier<(S - 2) * L>();
+            const int so = (t % S) * kStageAB;
+#pragma unroll
+            for (int i = 0; i < L; ++i) load(so, t + S, i);
+        }
+        __builtin_amdgcn_s_waitcnt(0);
+        lds_barrier();  // the MFMA waves' epilogue barrier; LDS is now theirs
+        return;
+    }
+
+    floatx4 acc[FN][FM];
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+        for (int i = 0; i < FM; ++i) acc[j][i] = floatx4{};
+    acc_fence(acc);
+
+    half8 af[2][FM];
+    half8 bf[2][FN];
+    auto read_frag = [&](int buf, int so, int ks, int r) {
+        if (r == 0)
+            bf[buf][0] = opb.read(smem, so, ks, 0);
+        else if (r <= FM)
+            af[buf][r - 1] = opa.read(smem, so, ks, r - 1);
+        else
+            bf[buf][r - FM] = opb.read(smem, so, ks, r - FM);
+    };
+
+    // Prologue: K-tiles 0 .. S-1 into the S stages (the loading waves), then
+    // K-tile 0's first fragments.
+    if constexpr (!PROD) {
+        for (int s = 0; s < S; ++s)
+#pragma unroll
+            for (int i = 0; i < L; ++i) load(s * kStageAB, s, i);
+        vm_barrier<(S - 1) * L>();
+    } else {
+        vm_barrier<0>();
+    }
+#pragma unroll
+    for (int r = 0; r < NR; ++r) read_frag(0, 0, 0, r);
+
+    constexpr int kBarAt = 4 < NM ? 4 : NM - 1;
+    // k step `step` (0 .. kBlk KS - 1 of the block) of K-tile t = t0 + step / KS
+    auto k_step = [&](auto step_c, int t0) {
+        constexpr int step = decltype(step_c)::value;
+        constexpr int tb = step / KS, ks = step % KS, cur = step & 1;
+        constexpr int s = tb % S, sn = (tb + 1) % S;
+        constexpr bool last = ks == KS - 1;
+        const int t = t0 + tb;
+        opa.refresh_lds();
+        opb.refresh_lds();
+        static_range<0, NM>([&](auto m_c) {
+            constexpr int m = decltype(m_c)::value;
+            constexpr int j = m / FM, i = (j & 1) ? FM - 1 - m % FM : m % FM;
+            mfma16_tied(bf[cur][j], af[cur][i], acc[j][i]);
+            if constexpr (!last) {
+                // the next k step's fragments, same stage
+                static_range<m * NR / NM, (m + 1) * NR / NM>(
+                    [&](auto r_c) { read_frag(cur ^ 1, s * kStageAB, ks + 1, decltype(r_c)::value); });
+            } else {
+                if constexpr (m == kBarAt) {
+                    // this wave's reads of stage s are done and (loading
+                    // waves) its loads of K-tile t + 1 are in LDS: after them
+                    // went out those of K-tiles t + 2 .. t + S - 1
+                    if constexpr (PROD)
+                        lgkm_barrier();
+                    else
+                        vm_barrier<(S - 2) * L>();
+                }
+                if constexpr (m >= kBarAt) {
+                    constexpr int q = m - kBarAt, slots = NM - kBarAt;
+                    // K-tile t + 1's first fragments from the next stage
+                    static_range<q * NR / slots, (q + 1) * NR / slots>(
+                        [&](auto r_c) { read_frag(cur ^ 1, sn * kStageAB, 0, decltype(r_c)::value); });
+                    if constexpr (!PROD)  // K-tile t + S into the stage just released
+                        static_range<q * L / slots, (q + 1) * L / slots>(
+                            [&](auto o_c) { load(s * kStageAB, t + S, decltype(o_c)::value); });
+                }
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        });
+#pragma unroll
+        for (int j = 0; j < FN; ++j) asm volatile("" ::"v"(bf[cur][j]));
+#pragma unroll
+        for (int i = 0; i < FM; ++i) asm volatile("" ::"v"(af[cur][i]));
+    };
+    for (int t0 = 0; t0 < tpad; t0 += kBlk)
+        static_range<0, kBlk * KS>([&](auto step_c) { k_step(step_c, t0); });
+
+    __builtin_amdgcn_s_waitcnt(0);  // no load still writing LDS when C is staged there
+    acc_fence(acc);
+    store_tile<C, false, kLds>(acc, smem, p, m0, n0, wm, wn, wave, lane);
+}
+
 // ---- launch ----------------------------------------------------------------
 
 using Cfg256 = Cfg<256, 256, 2, 2>;   // 4 waves, 128x128 each
@@ -2155,6 +2395,44 @@ hipError_t launch(const Params &p, int g, int cus, hipStream_t stream) {
     }
 }
 
+// The ring kernel's variants (gemm_f16_options.variant 1..7): (block_k,
+// stages, loader waves).  A variant whose LDS does not fit, or whose MFMA
+// waves would not fit their registers next to loader waves, is not
+// compiled; the host refuses it before launching.
+template <class CD, int BK, int S, bool PROD>
+constexpr bool ring_fits() {
+    constexpr int stage = (CD::BM + CD::BN) * 2 * BK;
+    // with loader waves the MFMA waves have 256 registers: a 128x64 wave tile
+    // fits a 2-stage ring, a 3-stage one's extra stage addresses spill
+    return CD::MB == 16 && CD::kWaves == 4 && S * stage <= 160 * 1024 &&
+           (!PROD || CD::FM * CD::FN <= (S == 2 ? 32 : 16));
+}
+
+template <class CD, int BK, int S, bool PROD>
+hipError_t launch_ring_variant(const Params &p, hipStream_t stream) {
+    if constexpr (ring_fits<CD, BK, S, PROD>()) {
+        const dim3 grid((unsigned)((int64_t)p.num_m * p.num_n));
+        return launch_kernel(gemm_f16_ring_kernel<CD, BK, S, PROD>, grid, dim3(CD::kThreads * (PROD ? 2 : 1)),
+                             stream, p);
+    } else {
+        return hipErrorInvalidValue;
+    }
+}
+
+template <class CD>
+hipError_t launch_ring(int variant, const Params &p, hipStream_t stream) {
+    switch (variant) {
+        case 1: return launch_ring_variant<CD, 64, 2, false>(p, stream);
+        case 2: return launch_ring_variant<CD, 64, 3, false>(p, stream);
+        case 3: return launch_ring_variant<CD, 32, 2, false>(p, stream);
+        case 4: return launch_ring_variant<CD, 32, 3, false>(p, stream);
+        case 5: return launch_ring_variant<CD, 32, 4, false>(p, stream);
+        case 6: return launch_ring_variant<CD, 64, 2, true>(p, stream);
+        case 7: return launch_ring_variant<CD, 64, 3, true>(p, stream);
+        default: return hipErrorInvalidValue;
+    }
+}
+
 // One function per block tile, each in a translation unit of its own so the
 // kernels compile in parallel.  nn selects the contract (false: C fp16 =
 // A B^T; true: D fp32 = A B with B [K,N]); the 128x128 16x16x32 tile serves
@@ -2168,5 +2446,10 @@ hipError_t launch_128x128_m16(const Params &p, int g, int cus, hipStream_t s);
 hipError_t launch_64x64(bool nn, const Params &p, int g, int cus, hipStream_t s);
 hipError_t launch_64x128(bool nn, const Params &p, int g, int cus, hipStream_t s);
 hipError_t launch_128x64(bool nn, const Params &p, int g, int cus, hipStream_t s);
+// the ring kernel's variants on the 256x256, 256x128, 128x256 and 128x128 tiles
+hipError_t launch_ring_256x256(int variant, const Params &p, hipStream_t s);
+hipError_t launch_ring_256x128(int variant, const Params &p, hipStream_t s);
+hipError_t launch_ring_128x256(int variant, const Params &p, hipStream_t s);
+hipError_t launch_ring_128x128(int variant, const Params &p, hipStream_t s);
 
 }  // namespace gemm_f16

@@ -32,7 +32,7 @@ def kernel_source_hash() -> str:
     side, the kernel templates, the scheduler and the per-tile units)."""
     h = hashlib.sha256()
     names = ["gemm_f16.hip", "kernels.h", "tile_sched.h"] + sorted(
-        os.path.basename(p) for p in glob.glob(os.path.join(CSRC, "tile_*.hip")))
+        os.path.basename(p) for p in glob.glob(os.path.join(CSRC, "tile_*.hip")) + glob.glob(os.path.join(CSRC, "ring_*.hip")))
     for name in names:
         with open(os.path.join(CSRC, name), "rb") as f:
             h.update(f.read())

@@ -29,6 +29,9 @@ def main(argv=None) -> int:
     ap.add_argument("--rounds", type=int, default=3)
     ap.add_argument("--reps", type=int, default=10)
     ap.add_argument("--swizzles", default="1,4,8")
+    ap.add_argument("--variants", action="store_true",
+                    help="also time the kernel variants (block_k 32/64, 2-4 LDS stages, loader waves) "
+                         "on every block tile they fit, default rasterization")
     ap.add_argument("--data", action="store_true",
                     help="instead: time the automatic configuration on one shape (default 8192^3) "
                          "with different operand values (zeros, ones, {-8..8}/8, U[0,1], U[-1,1], N(0,1))")
@@ -62,7 +65,12 @@ def main(argv=None) -> int:
         B = (torch.rand((n, k), device="cuda", generator=gen) * 2 - 1).half()
         C = torch.empty((m, n), device="cuda", dtype=torch.float16)
         auto = g.select_tile(m, n, k)
-        opts = [(t, 0, -1) for t in sorted(g.TILES)] + [(auto, s, x) for s in swz for x in (0, 1)]
+        opts = [(t, 0, -1, 0) for t in sorted(g.TILES)] + [(auto, s, x, 0) for s in swz for x in (0, 1)]
+        if a.variants:
+            for v, (bk, _, _) in sorted(g.VARIANTS.items()):
+                for t in sorted(g.TILES):
+                    if k % bk == 0 and g.gemm_f16_nt_raw(0, 0, k, 16, 16, 16, 0, t, 0, -1, v) == g.OK:
+                        opts.append((t, 0, -1, v))
         times = {o: [] for o in opts}
         for _ in range(a.rounds):
             for o in opts:
@@ -85,8 +93,9 @@ def main(argv=None) -> int:
         for o in opts:
             us = statistics.median(times[o]) * 1e3
             tf = 2.0 * m * n * k / (us * 1e-6) / 1e12
-            print(json.dumps({"shape": [m, n, k], "tile": o[0], "swizzle": o[1], "xcd": o[2],
-                              "us": round(us, 2), "tflops": round(tf, 1), "auto": o[0] == auto}), flush=True)
+            print(json.dumps({"shape": [m, n, k], "tile": o[0], "swizzle": o[1], "xcd": o[2], "variant": o[3],
+                              "us": round(us, 2), "tflops": round(tf, 1),
+                              "auto": o[0] == auto and o[3] == 0}), flush=True)
             if best is None or us < best[1]:
                 best = (o, us)
         print(json.dumps({"shape": [m, n, k], "best": best[0], "best_us": round(best[1], 2),

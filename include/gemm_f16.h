@@ -76,16 +76,38 @@ int gemm_f16_nt(int64_t m, int64_t n, int64_t k, const void *a, const void *b,
  *            "Tile Rasterization"); 0 = library default, 1 = plain grid.
  *   xcd      1 = give each of the 8 XCDs a contiguous run of tiles,
  *            0 = hardware dispatch order, -1 = library default.
- * Every option changes only the schedule: the fp32 sum of each output is
- * taken in the same order, so results are bitwise identical across options
- * that select the same block tile.
+ *   variant  0 = the library's kernels.  1..7 = a kernel whose K-tile width
+ *            (block_k), LDS ring depth and wave roles are those of the
+ *            GEMM_F16_VARIANT_* below, one tile per workgroup (the tuning
+ *            sweep's axes; "4. Pipeline Abstraction and Two Consumer Warp
+ *            Groups", sections "Pipeline Depth" and "Two Consumer Warp
+ *            Groups").  A variant needs C = A B^T, an explicit block tile of
+ *            256x256 (variants 1, 3, 4, 5 only), 256x128 or 128x256 (not
+ *            variant 7), or 128x128, K a positive multiple of its block_k,
+ *            and 16-byte aligned A and B; otherwise the call returns
+ *            GEMM_F16_EINVAL.
+ * Every option but the variant changes only the schedule: the fp32 sum of
+ * each output is taken in the same order, so results are bitwise identical
+ * across options that select the same block tile.
  */
 typedef struct {
     int32_t tile;
     int32_t swizzle;
     int32_t xcd;
-    int32_t reserved;
+    int32_t variant;
 } gemm_f16_options;
+
+enum {
+    GEMM_F16_VARIANT_DEFAULT = 0,
+    GEMM_F16_VARIANT_BK64_S2 = 1,      /* block_k 64, 2 LDS stages, every wave loads */
+    GEMM_F16_VARIANT_BK64_S3 = 2,      /* block_k 64, 3 stages */
+    GEMM_F16_VARIANT_BK32_S2 = 3,      /* block_k 32, 2 stages */
+    GEMM_F16_VARIANT_BK32_S3 = 4,      /* block_k 32, 3 stages */
+    GEMM_F16_VARIANT_BK32_S4 = 5,      /* block_k 32, 4 stages */
+    GEMM_F16_VARIANT_PRODUCER_S2 = 6,  /* block_k 64, 2 stages, 4 loader waves + 4 MFMA waves */
+    GEMM_F16_VARIANT_PRODUCER_S3 = 7,  /* block_k 64, 3 stages, 4 loader waves + 4 MFMA waves */
+    GEMM_F16_VARIANT_LAST = 7
+};
 
 enum {
     GEMM_F16_TILE_AUTO = 0,

@@ -3,6 +3,7 @@ host logic (argument checks, status strings, tile scheduler, tile choice)
 behaves as documented.  No GPU is needed: every call here returns before the
 library makes its first HIP call.
 """
+import ctypes
 import os
 import re
 import subprocess
@@ -161,3 +162,25 @@ def test_argument_errors_come_before_the_device_gate():
     env = dict(os.environ, GEMM_F16_TEST_ARCH="gfx942", PYTHONPATH=ROOT)
     out = subprocess.run([sys.executable, "-c", code], env=env, capture_output=True, text=True, check=True)
     assert [int(x) for x in out.stdout.split()] == [g.EINVAL, g.OK]
+
+
+@pytest.mark.parametrize("tile,variant,k,a_off", [
+    (0, 1, 64, 0),                    # variants need an explicit block tile
+    (3, 1, 64, 0),                    # ... of 256x256, 256x128, 128x256 or 128x128
+    (g.TILE_256x256, 2, 64, 0),       # 3 stages of block_k 64 do not fit 256x256's LDS
+    (g.TILE_256x256, 6, 64, 0),       # loader waves: the MFMA waves' 128x128 would not fit
+    (g.TILE_256x128, 7, 64, 0),       # 3 stages with loader waves: 128x128 only
+    (g.TILE_128x128, 1, 96, 0),       # K a multiple of block_k 64
+    (g.TILE_128x128, 3, 48, 0),       # ... of block_k 32
+    (g.TILE_128x128, 1, 0, 0),        # K > 0
+    (g.TILE_128x128, 1, 64, 8),       # 16-byte aligned operands
+    (g.TILE_128x128, 8, 64, 0),       # no variant 8
+    (g.TILE_128x128, -1, 64, 0),
+])
+def test_bad_variants_rejected(tile, variant, k, a_off):
+    assert g.gemm_f16_nt_raw(8, 8, k, FAKE_A + a_off, FAKE_B, FAKE_C, 0, tile, 0, -1, variant) == g.EINVAL
+
+
+def test_variants_are_for_the_first_contract():
+    opt = g.Options(g.TILE_128x128, 0, -1, 1)
+    assert g.lib().gemm_f16_nn_f32_ex(8, 8, 64, FAKE_A, FAKE_B, FAKE_C, None, ctypes.byref(opt)) == g.EINVAL

@@ -465,3 +465,35 @@ def test_overlap_and_null_are_refused_on_device():
     x = torch.zeros(64 * 64, dtype=torch.float16, device="cuda")
     assert g.gemm_f16_nt_raw(64, 64, 64, x.data_ptr(), x.data_ptr(), x.data_ptr()) == g.EOVERLAP
     assert g.gemm_f16_nt_raw(64, 64, 64, 0, x.data_ptr(), x.data_ptr()) == g.ENULL
+
+
+# The tuning variants (options.variant): block_k 32 / 64, 2 to 4 LDS stages,
+# and 4 loader waves beside the 4 MFMA waves, on every tile they fit.  One
+# tile per workgroup; the K-tile count is padded with all-zero K-tiles to a
+# whole unrolled block (K = one K-tile up to well past it, ragged M and N).
+VARIANT_TILES = {g.TILE_256x256: (1, 3, 4, 5), g.TILE_256x128: (1, 2, 3, 4, 5, 6),
+                 g.TILE_128x256: (1, 2, 3, 4, 5, 6), g.TILE_128x128: (1, 2, 3, 4, 5, 6, 7)}
+VARIANT_CASES = [(tile, v) for tile, vs in VARIANT_TILES.items() for v in vs]
+
+
+@pytest.mark.parametrize("tile,variant", VARIANT_CASES)
+def test_variants_bit_exact(tile, variant):
+    bk = g.VARIANTS[variant][0]
+    rng = np.random.default_rng(tile * 10 + variant)
+    for m, n, k in [(300, 520, bk), (513, 260, 5 * bk), (700, 900, 13 * bk)]:
+        _announce("variant", tile, variant, m, n, k)
+        a = (rng.integers(-8, 9, size=(m, k)) / 8).astype(np.float16)
+        b = (rng.integers(-8, 9, size=(n, k)) / 8).astype(np.float16)
+        assert_bits_equal(run_gemm(a, b, tile=tile, variant=variant), oracle.gemm_f16_nt(a, b),
+                          f"variant {variant} tile {tile} {m}x{n}x{k}")
+
+
+@pytest.mark.parametrize("variant", [1, 4, 6])
+def test_variants_random_operands(variant):
+    """uniform[-1,1] operands, 1024x1024x2048 on the 128x128 tile: ulp bar."""
+    _announce("variant random", variant)
+    rng = np.random.default_rng(variant)
+    a = rng.uniform(-1, 1, (1024, 2048)).astype(np.float16)
+    b = rng.uniform(-1, 1, (1024, 2048)).astype(np.float16)
+    assert_ulp(run_gemm(a, b, tile=g.TILE_128x128, variant=variant), oracle.gemm_f16_nt(a, b), 2048,
+               f"variant {variant}")
