@@ -226,6 +226,42 @@ def child(args) -> int:
     return 0
 
 
+def profile_run(args) -> int:
+    """W warm-up steps and K event-timed steps of one workload in this process,
+    so that a profiler wrapped around it sees exactly those W + K launches."""
+    import numpy as np
+    import torch
+
+    import dense_fp16_gemm_f16_amd as g
+    from dense_fp16_gemm_f16_amd import inputs
+
+    w = inputs.WORKLOADS[args.workload]
+    a_np, b_np = inputs.workload_inputs(w.name)
+    dev = torch.device("cuda:0")
+    a = torch.from_numpy(a_np).to(dev)
+    b = torch.from_numpy(b_np).to(dev)
+    nn = w.b_layout == "kn"
+    c = torch.empty((w.m, w.n), dtype=torch.float32 if nn else torch.float16, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    call = g.gemm_f16_nn_f32_raw if nn else g.gemm_f16_nt_raw
+    for i in range(args.warmup + args.steps):
+        if i == args.warmup:
+            torch.cuda.synchronize()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+        rc = call(w.m, w.n, w.k, a.data_ptr(), b.data_ptr(), c.data_ptr(), stream.cuda_stream,
+                  args.tile, args.swizzle, args.xcd)
+        if rc != g.OK:
+            raise g.GemmError(rc)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    us = e0.elapsed_time(e1) * 1e3 / max(args.steps, 1)
+    print(json.dumps({"workload": w.name, "steps": args.steps, "warmup": args.warmup, "us_per_step": round(us, 2),
+                      "tflops": round(w.flops / (us * 1e-6) / 1e12, 1)}), flush=True)
+    return 0
+
+
 # ---- parent: inputs, children, oracle ------------------------------------------------
 
 def cpu_baseline(a, b, c_gpu, w, budget_s: float):
@@ -288,6 +324,9 @@ def main() -> int:
     ap.add_argument("--traffic-calibration", type=int, default=0, metavar="BYTES",
                     help="only run a plain elementwise copy (negation) of BYTES, 3 times: the "
                          "reference for scaling rocprofv3 FETCH_SIZE / WRITE_SIZE")
+    ap.add_argument("--profile", action="store_true",
+                    help="for a profiler: this process alone runs the workload's W + K steps and nothing else "
+                         "(no children, no other workloads, no CPU baseline)")
     ap.add_argument("--child", default=None, help=argparse.SUPPRESS)
     ap.add_argument("--index", type=int, default=0, help=argparse.SUPPRESS)
     args = ap.parse_args()
@@ -298,6 +337,8 @@ def main() -> int:
         return 2
     if args.child:
         return child(args)
+    if args.profile:
+        return profile_run(args)
 
     if args.traffic_calibration:
         import torch

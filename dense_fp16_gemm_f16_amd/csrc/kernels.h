@@ -139,9 +139,10 @@ constexpr uint32_t kOutOfRange = 0x80000000u;  // buffer offset past any num_rec
 #ifndef GEMM_STREAM
 #define GEMM_STREAM 1
 #endif
-// 1: the stream kernel's store units run p (column pair) fastest
+// 0: the stream kernel's store units run i (row block) fastest; 1: p
+// (column pair) fastest, the two halves of a C line back to back
 #ifndef GEMM_UNIT_P_FAST
-#define GEMM_UNIT_P_FAST 1
+#define GEMM_UNIT_P_FAST 0
 #endif
 // 1: the stream kernel's stores carry the streaming hint where C's rows are
 // whole 128-byte lines
@@ -1893,8 +1894,10 @@ void gemm_f16_stream_kernel(const Params p) {
             opb.template load_tile<S>(smem, next ? nxt.b : cur.b, next ? nxt.b_bytes : cur.b_bytes, t, i - LA);
     };
 
-    // Unit u = (p, i): p fastest, so the units that write the two 64-byte
-    // halves of a 128-byte line of C (p = 2c, 2c + 1) go out back to back.
+    // Unit u = (p, i), i fastest by default: step 0 of a tile's first K-tile
+    // then keeps one pair of B fragments for FM units in a row.  (p fastest
+    // puts the two 64-byte halves of a 128-byte line of C, p = 2c and 2c + 1,
+    // back to back; it measured 1-3% slower.)
     constexpr auto unit_p = [](int u) { return GEMM_UNIT_P_FAST ? u % (FN / 2) : u / FM; };
     constexpr auto unit_i = [](int u) { return GEMM_UNIT_P_FAST ? u / (FN / 2) : u % FM; };
     // Store unit u of tile t: lane l holds row 16 i + l % 16 of the wave's

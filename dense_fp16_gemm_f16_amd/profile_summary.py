@@ -1,6 +1,7 @@
 """Summaries of rocprofv3 CSV output for the GEMM kernel.
 
     python -m dense_fp16_gemm_f16_amd.profile_summary stats DIR [--kernel gemm_f16_nt_kernel]
+    python -m dense_fp16_gemm_f16_amd.profile_summary window DIR --kernel NAME [--min-us X] --skip N --count K
     python -m dense_fp16_gemm_f16_amd.profile_summary traffic \\
         --gemm-fetch DIR --gemm-write DIR --copy-fetch DIR --copy-write DIR \\
         --copy-bytes N --workload NAME --out profiles/traffic_NAME.json
@@ -55,6 +56,21 @@ def kernel_stats(d: str, kernel: str) -> dict:
     raise KeyError(kernel)
 
 
+def kernel_window(d: str, kernel: str, min_us: float, skip: int, count: int) -> dict:
+    """Durations of the launches of `kernel` lasting at least min_us, in dispatch
+    order, after the first `skip` of them: `count` launches."""
+    path = _one(os.path.join(d, "**", "*kernel_trace.csv"))
+    rows = [r for r in csv.DictReader(open(path)) if kernel in r["Kernel_Name"]]
+    rows.sort(key=lambda r: int(r["Start_Timestamp"]))
+    durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in rows]
+    durs = [x for x in durs if x >= min_us]
+    sel = durs[skip:skip + count]
+    if len(sel) != count:
+        raise ValueError(f"only {len(sel)} of {count} launches after skipping {skip}")
+    return {"kernel": kernel, "launches": count, "avg_us": statistics.mean(sel), "median_us": statistics.median(sel),
+            "min_us": min(sel), "max_us": max(sel)}
+
+
 def counter_per_dispatch(d: str, kernel: str, counter: str) -> list[float]:
     path = _one(os.path.join(d, "**", "*counter_collection.csv"))
     per = {}
@@ -70,6 +86,12 @@ def main(argv=None) -> int:
     s1 = sub.add_parser("stats")
     s1.add_argument("dir")
     s1.add_argument("--kernel", default="gemm_f16_nt_kernel")
+    s3 = sub.add_parser("window", help="launches of one kernel from a kernel trace, selected by position")
+    s3.add_argument("dir")
+    s3.add_argument("--kernel", required=True)
+    s3.add_argument("--min-us", type=float, default=0.0, help="only launches at least this long")
+    s3.add_argument("--skip", type=int, default=0, help="matching launches to skip first")
+    s3.add_argument("--count", type=int, required=True, help="matching launches to take after them")
     s2 = sub.add_parser("traffic")
     for k in ("gemm-fetch", "gemm-write", "copy-fetch", "copy-write", "workload", "out"):
         s2.add_argument("--" + k, required=True)
@@ -80,6 +102,9 @@ def main(argv=None) -> int:
     a = ap.parse_args(argv)
     if a.cmd == "stats":
         print(json.dumps(kernel_stats(a.dir, a.kernel)))
+        return 0
+    if a.cmd == "window":
+        print(json.dumps(kernel_window(a.dir, a.kernel, a.min_us, a.skip, a.count)))
         return 0
     fetch = counter_per_dispatch(a.gemm_fetch, a.kernel, "FETCH_SIZE")
     write = counter_per_dispatch(a.gemm_write, a.kernel, "WRITE_SIZE")
