@@ -4,8 +4,10 @@ The kernels are compiled per block tile (csrc/tile_*.hip, each instantiating
 the templates of csrc/kernels.h) and the host side (csrc/gemm_f16.hip) on its
 own, all in parallel, then linked into one shared library.
 
-build_ceiling() builds the MFMA-rate probe libmfma_ceiling.so, a measurement
-tool that is not part of the library (tune.py --ceiling builds it on demand).
+build_ceiling() builds the MFMA-rate probe libmfma_ceiling.so, and
+build_trace() the timestamp-traced copy of the library, libgemm_f16_trace.so
+(the same sources with -DGEMM_F16_TRACE): measurement tools that are not part
+of the library (tune.py --ceiling and trace.py build them on demand).
 """
 from __future__ import annotations
 
@@ -21,6 +23,8 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libgemm_f16.so")
 OBJ_DIR = os.path.join(HERE, "_build")
+TRACE_LIB = os.path.join(HERE, "libgemm_f16_trace.so")
+TRACE_OBJ_DIR = os.path.join(HERE, "_build_trace")
 CEILING_SRC = os.path.join(CSRC, "mfma_ceiling.hip")
 CEILING_LIB = os.path.join(HERE, "libmfma_ceiling.so")
 
@@ -52,21 +56,30 @@ def _run(cmd: list[str], verbose: bool) -> None:
     subprocess.run(cmd, check=True)
 
 
-def build(verbose: bool = False, extra: list[str] | None = None, jobs: int | None = None) -> str:
-    """Compile every translation unit (in parallel) and link libgemm_f16.so."""
-    os.makedirs(OBJ_DIR, exist_ok=True)
+def _build_lib(lib: str, obj_dir: str, flags: list[str], verbose: bool, jobs: int | None) -> str:
+    os.makedirs(obj_dir, exist_ok=True)
     srcs = sources()
-    objs = [os.path.join(OBJ_DIR, os.path.splitext(os.path.basename(s))[0] + ".o") for s in srcs]
-    cmds = [[_hipcc(), *HIPCC_FLAGS, *(extra or []), "-I", INCLUDE, "-I", CSRC, "-c", s, "-o", o]
+    objs = [os.path.join(obj_dir, os.path.splitext(os.path.basename(s))[0] + ".o") for s in srcs]
+    cmds = [[_hipcc(), *HIPCC_FLAGS, *flags, "-I", INCLUDE, "-I", CSRC, "-c", s, "-o", o]
             for s, o in zip(srcs, objs)]
     jobs = jobs or min(len(cmds), 16, os.cpu_count() or 1)
     with concurrent.futures.ThreadPoolExecutor(max_workers=jobs) as ex:
         for f in [ex.submit(_run, c, verbose) for c in cmds]:
             f.result()
-    tmp = LIB + ".tmp"
+    tmp = lib + ".tmp"
     _run([_hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *objs, "-o", tmp], verbose)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
+
+
+def build(verbose: bool = False, extra: list[str] | None = None, jobs: int | None = None) -> str:
+    """Compile every translation unit (in parallel) and link libgemm_f16.so."""
+    return _build_lib(LIB, OBJ_DIR, list(extra or []), verbose, jobs)
+
+
+def build_trace(verbose: bool = False, jobs: int | None = None) -> str:
+    """The timestamp-traced copy of the library (measurement tool)."""
+    return _build_lib(TRACE_LIB, TRACE_OBJ_DIR, ["-DGEMM_F16_TRACE"], verbose, jobs)
 
 
 def build_ceiling(verbose: bool = False) -> str:
@@ -78,4 +91,7 @@ def build_ceiling(verbose: bool = False) -> str:
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    if "--trace" in sys.argv[1:]:
+        print(build_trace(verbose=True))
+    else:
+        print(build(verbose=True))

@@ -158,6 +158,49 @@ constexpr uint32_t kOutOfRange = 0x80000000u;  // buffer offset past any num_rec
 #define GEMM_STAGE_SETS 1
 #endif
 
+// Timestamp trace (built only with -DGEMM_F16_TRACE, a profiling build of
+// the library, never the library itself): the fragment-ahead and stream
+// kernels record per wave, in this translation unit's copy of gemm_trace,
+// the shader-clock counter (s_memtime) at their start, after the prologue's
+// wait, after the K loop and after their last store has completed, the
+// 100 MHz counter (s_memrealtime) at start and end, the cycles spent in the
+// release and acquire barriers of the K loop, the start of each of the
+// first six tiles (stream kernel), and the XCC and HW_ID registers.  Slots
+// of 20 words per wave, wave w of workgroup b at (4 b + w) * 20; workgroups
+// past kTraceBlocks and waves past the fourth record nothing.
+#ifdef GEMM_F16_TRACE
+constexpr int kTraceBlocks = 2048, kTraceWords = 20;
+static __device__ unsigned long long gemm_trace[kTraceBlocks * 4 * kTraceWords];
+__device__ __forceinline__ uint64_t trace_clock() { return __builtin_amdgcn_s_memtime(); }
+__device__ __forceinline__ uint64_t trace_realtime() { return __builtin_amdgcn_s_memrealtime(); }
+struct TraceRecord {
+    uint64_t t0 = 0, t1 = 0, rel = 0, acq = 0, acq_first = 0, tl = 0, r0 = 0, tiles = 0;
+    uint64_t tile_start[6] = {0, 0, 0, 0, 0, 0};
+};
+__device__ __forceinline__ void trace_write(const TraceRecord &r, int wave, int lane) {
+    const uint64_t te = trace_clock(), re = trace_realtime();
+    if (lane != 0 || wave >= 4 || blockIdx.x >= (unsigned)kTraceBlocks) return;
+    unsigned long long *q = gemm_trace + ((size_t)blockIdx.x * 4 + wave) * kTraceWords;
+    q[0] = r.t0;
+    q[1] = r.t1;
+    q[2] = r.rel;
+    q[3] = r.acq;
+    q[4] = r.acq_first;
+    q[5] = r.tl;
+    q[6] = te;
+    q[7] = r.r0;
+    q[8] = re;
+    q[9] = r.tiles;
+#pragma unroll
+    for (int i = 0; i < 6; ++i) q[10 + i] = r.tile_start[i];
+    q[16] = (unsigned)__builtin_amdgcn_s_getreg(20 | (3 << 11));  // XCC_ID[3:0]
+    q[17] = (unsigned)__builtin_amdgcn_s_getreg(4 | (31 << 11));  // HW_ID
+}
+#define GEMM_TRACE_DO(...) __VA_ARGS__
+#else
+#define GEMM_TRACE_DO(...)
+#endif
+
 struct Params {
     const _Float16 *a;
     const _Float16 *b;
@@ -1310,6 +1353,7 @@ void gemm_f16_direct_ahead_kernel(const Params p) {
                   "LDS immediates must fit the 16-bit offset field");
     __shared__ __attribute__((aligned(1024))) char smem[kLds];
 
+    GEMM_TRACE_DO(TraceRecord tr; tr.t0 = trace_clock(); tr.r0 = trace_realtime(); tr.tiles = 1;)
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -1371,6 +1415,7 @@ void gemm_f16_direct_ahead_kernel(const Params p) {
 #pragma unroll
     for (int i = 0; i < L; ++i) load(S1{}, 1, i);
     vm_barrier<L>();
+    GEMM_TRACE_DO(tr.t1 = trace_clock();)
 #pragma unroll
     for (int r = 0; r < NR; ++r) read_frag(0, 0, 0, r);
 #pragma unroll
@@ -1386,7 +1431,11 @@ void gemm_f16_direct_ahead_kernel(const Params p) {
             constexpr int m = decltype(m_c)::value;
             constexpr int j = m / FM, i = (j & 1) ? FM - 1 - m % FM : m % FM;
             mfma16_tied(bf[0][j], af[0][i], acc[j][i]);
-            if constexpr (m == kRelAt) lgkm_barrier();
+            if constexpr (m == kRelAt) {
+                GEMM_TRACE_DO(const uint64_t tb = trace_clock();)
+                lgkm_barrier();
+                GEMM_TRACE_DO(tr.rel += trace_clock() - tb;)
+            }
             if constexpr (m >= kRelAt) {
                 constexpr int q = m - kRelAt, slots = NM - kRelAt;
                 static_range<q * L0 / slots, (q + 1) * L0 / slots>(
@@ -1403,7 +1452,11 @@ void gemm_f16_direct_ahead_kernel(const Params p) {
             constexpr int m = decltype(m_c)::value;
             constexpr int j = m / FM, i = (j & 1) ? FM - 1 - m % FM : m % FM;
             mfma16_tied(bf[B1][j], af[B1][i], acc[j][i]);
-            if constexpr (m == kAcqAt) vm_only_barrier<L0>();
+            if constexpr (m == kAcqAt) {
+                GEMM_TRACE_DO(const uint64_t tb = trace_clock();)
+                vm_only_barrier<L0>();
+                GEMM_TRACE_DO(tr.acq += trace_clock() - tb;)
+            }
             if constexpr (m >= kAcqAt) {
                 constexpr int nl = L - L0, total = 2 * NR + nl, slots = NM - kAcqAt, q = m - kAcqAt;
                 // R R L R R L ...: the reads first while both remain
@@ -1439,8 +1492,10 @@ void gemm_f16_direct_ahead_kernel(const Params p) {
     if (kt < kt_count) k_iter(S0{}, kt);
 
     vm_barrier<0>();  // no load is still writing LDS when the epilogue stages C there
+    GEMM_TRACE_DO(tr.tl = trace_clock();)
     acc_fence(acc);
     store_tile<C, NN, kLds>(acc, smem, p, m0, n0, wm, wn, wave, lane);
+    GEMM_TRACE_DO(__builtin_amdgcn_s_waitcnt(0); trace_write(tr, wave, lane);)
 }
 
 // The fragment-ahead kernel with one workgroup per CU walking several tiles
@@ -1798,6 +1853,7 @@ void gemm_f16_stream_kernel(const Params p) {
                   "LDS immediates must fit the 16-bit offset field");
     __shared__ __attribute__((aligned(1024))) char smem[kLds];
 
+    GEMM_TRACE_DO(TraceRecord tr; tr.t0 = trace_clock(); tr.r0 = trace_realtime();)
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
     const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
@@ -1946,6 +2002,7 @@ void gemm_f16_stream_kernel(const Params p) {
 #pragma unroll
     for (int i = 0; i < L; ++i) load(S1{}, 1, i);
     vm_barrier<0>();
+    GEMM_TRACE_DO(tr.t1 = trace_clock();)
 #pragma unroll
     for (int r = 0; r < NR; ++r) read_frag(0, 0, 0, r);
 #pragma unroll
@@ -1973,7 +2030,11 @@ void gemm_f16_stream_kernel(const Params p) {
                 constexpr int j = m / FM, i = (j & 1) ? FM - 1 - m % FM : m % FM;
                 mfma16_tied(bf[0][j], af[0][i], acc[j][i]);
             }
-            if constexpr (m == kRelAt) lgkm_barrier();
+            if constexpr (m == kRelAt) {
+                GEMM_TRACE_DO(const uint64_t tb = trace_clock();)
+                lgkm_barrier();
+                GEMM_TRACE_DO(tr.rel += trace_clock() - tb;)
+            }
             if constexpr (m >= kRelAt) {
                 constexpr int q = m - kRelAt, slots = NM - kRelAt;
                 static_range<q * L0 / slots, (q + 1) * L0 / slots>(
@@ -1993,7 +2054,11 @@ void gemm_f16_stream_kernel(const Params p) {
             // Acquire: this wave's loads of K-tile t+1 are in LDS; after
             // them went out the loads of K-tile t+2 of step 0 and, in a
             // tile's first K-tile, the previous tile's U stores.
-            if constexpr (m == kAcqAt) vm_only_barrier<FIRST ? U + L0 : L0>();
+            if constexpr (m == kAcqAt) {
+                GEMM_TRACE_DO(const uint64_t tb = trace_clock();)
+                vm_only_barrier<FIRST ? U + L0 : L0>();
+                GEMM_TRACE_DO(const uint64_t dt = trace_clock() - tb; tr.acq += dt; if constexpr (FIRST) tr.acq_first += dt;)
+            }
             if constexpr (m >= kAcqAt) {
                 constexpr int nl = L - L0, total = 2 * NR + nl, slots = NM - kAcqAt, q = m - kAcqAt;
                 // R R L R R L ...: the reads first while both remain
@@ -2027,6 +2092,15 @@ void gemm_f16_stream_kernel(const Params p) {
     // reads the fragments of a "next tile" past the grid, zeros.
     __amdgpu_buffer_rsrc_t rc_prv = make_rsrc(prv.c, 0u);
     for (;;) {
+#ifdef GEMM_F16_TRACE
+        {
+            const uint64_t ts = trace_clock();
+#pragma unroll
+            for (int i = 0; i < 6; ++i)
+                if (tr.tiles == (uint64_t)i) tr.tile_start[i] = ts;  // constant indexes: no scratch
+            ++tr.tiles;
+        }
+#endif
         k_iter(S0{}, 0, T{}, prv, rc_prv);
         k_iter(S1{}, 1, F{}, prv, rc_prv);
         for (int kt = 2; kt < kt_count; kt += 2) {
@@ -2041,6 +2115,7 @@ void gemm_f16_stream_kernel(const Params p) {
         nxt = tile_rows(idx + G);
     }
     // the last tile's units
+    GEMM_TRACE_DO(tr.tl = trace_clock();)
     acc_fence(acc);
     {
         const __amdgpu_buffer_rsrc_t rc = make_rsrc(cur.c, cur.c_bytes);
@@ -2052,6 +2127,7 @@ void gemm_f16_stream_kernel(const Params p) {
     // the last tile's loads past the tile (zeros into LDS) and its stores
     // are done before the workgroup ends
     __builtin_amdgcn_s_waitcnt(0);
+    GEMM_TRACE_DO(trace_write(tr, wave, lane);)
 }
 
 // ---- configurable ring (the tuning sweep's other axes) -------------------------
