@@ -288,7 +288,11 @@ int gemm_f16_tile_coord(int64_t pid, int64_t num_m, int64_t num_n, int32_t swizz
     if (num_m < 1 || num_n < 1 || swizzle < 1 || pid < 0 || pid >= num_m * num_n)
         return GEMM_F16_EINVAL;
     if (!m_block || !n_block) return GEMM_F16_ENULL;
-    const TileCoord t = tile_coord(pid, num_m, num_n, swizzle, xcd != 0);
+    // grids the kernels run (below 2^31 tiles) take their 32-bit arithmetic
+    const TileCoord t = num_m * num_n < (int64_t(1) << 31)
+                            ? tile_coord<uint32_t>((uint32_t)pid, (uint32_t)num_m, (uint32_t)num_n,
+                                                   (uint32_t)swizzle, xcd != 0)
+                            : tile_coord<int64_t>(pid, num_m, num_n, swizzle, xcd != 0);
     *m_block = t.m_block;
     *n_block = t.n_block;
     return GEMM_F16_OK;

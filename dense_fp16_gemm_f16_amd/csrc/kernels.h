@@ -712,7 +712,7 @@ void gemm_f16_kernel(const Params p) {
     const int wm = wave / C::WN;
     const int wn = wave % C::WN;
 
-    const TileCoord tc = tile_coord(blockIdx.x, p.num_m, p.num_n, p.swizzle, p.xcd != 0);
+    const TileCoord tc = tile_coord<uint32_t>(blockIdx.x, p.num_m, p.num_n, p.swizzle, p.xcd != 0);
     const int m0 = (int)tc.m_block * BM;
     const int n0 = (int)tc.n_block * BN;
     const int kt_count = p.k_tiles;
@@ -1165,7 +1165,7 @@ void gemm_f16_direct_kernel(const Params p) {
     const int wm = wave / C::WN;
     const int wn = wave % C::WN;
 
-    const TileCoord tc = tile_coord(blockIdx.x, p.num_m, p.num_n, p.swizzle, p.xcd != 0);
+    const TileCoord tc = tile_coord<uint32_t>(blockIdx.x, p.num_m, p.num_n, p.swizzle, p.xcd != 0);
     const int m0 = (int)tc.m_block * BM;
     const int n0 = (int)tc.n_block * BN;
     const int kt_count = p.k_tiles;
@@ -1360,7 +1360,7 @@ void gemm_f16_direct_ahead_kernel(const Params p) {
     const int wm = wave / C::WN;
     const int wn = wave % C::WN;
 
-    const TileCoord tc = tile_coord(blockIdx.x, p.num_m, p.num_n, p.swizzle, p.xcd != 0);
+    const TileCoord tc = tile_coord<uint32_t>(blockIdx.x, p.num_m, p.num_n, p.swizzle, p.xcd != 0);
     const int m0 = (int)tc.m_block * BM;
     const int n0 = (int)tc.n_block * BN;
     const int kt_count = p.k_tiles;
@@ -1563,7 +1563,7 @@ void gemm_f16_persistent_kernel(const Params p) {
     auto tile_rows = [&](int id) {
         TileRows r;
         if (id < ntiles) {
-            const TileCoord tc = tile_coord(id, p.num_m, p.num_n, p.swizzle, p.xcd != 0);
+            const TileCoord tc = tile_coord<uint32_t>(id, p.num_m, p.num_n, p.swizzle, p.xcd != 0);
             r.m0 = (int)tc.m_block * BM;
             r.n0 = (int)tc.n_block * BN;
             const uint32_t rows_a = (uint32_t)min(BM, p.m - r.m0), rows_b = (uint32_t)min(BN, p.n - r.n0);
@@ -1876,7 +1876,7 @@ void gemm_f16_stream_kernel(const Params p) {
     auto tile_rows = [&](int id) {
         TileRows r;
         if (id < ntiles) {
-            const TileCoord tc = tile_coord(id, p.num_m, p.num_n, p.swizzle, p.xcd != 0);
+            const TileCoord tc = tile_coord<uint32_t>(id, p.num_m, p.num_n, p.swizzle, p.xcd != 0);
             const int m0 = (int)tc.m_block * BM;
             r.n0 = (int)tc.n_block * BN;
             const uint32_t rows_a = (uint32_t)min(BM, p.m - m0), rows_b = (uint32_t)min(BN, p.n - r.n0);
@@ -2246,7 +2246,7 @@ void gemm_f16_ring_kernel(const Params p) {
     const int wm = (wave % NC) / C::WN;
     const int wn = (wave % NC) % C::WN;
 
-    const TileCoord tc = tile_coord(blockIdx.x, p.num_m, p.num_n, p.swizzle, p.xcd != 0);
+    const TileCoord tc = tile_coord<uint32_t>(blockIdx.x, p.num_m, p.num_n, p.swizzle, p.xcd != 0);
     const int m0 = (int)tc.m_block * BM;
     const int n0 = (int)tc.n_block * BN;
     const int kt = p.k / BK;                      // K % BK == 0 (the host's condition)

@@ -30,12 +30,16 @@ namespace gemm_f16 {
 
 constexpr int kNumXcd = 8;
 
-// Dispatch index -> logical index (bijection on [0, grid)).
-GEMM_HD int64_t xcd_remap(int64_t pid, int64_t grid) {
-    const int64_t q = grid / kNumXcd;
-    const int64_t r = grid % kNumXcd;
-    const int64_t x = pid % kNumXcd;
-    const int64_t start = x * q + (x < r ? x : r);
+// Dispatch index -> logical index (bijection on [0, grid)).  I: the integer
+// type of the arithmetic (the kernels take uint32_t: the host refuses grids
+// of 2^31 tiles or more, and 64-bit division is a long instruction sequence
+// on the GPU).
+template <class I>
+GEMM_HD I xcd_remap(I pid, I grid) {
+    const I q = grid / kNumXcd;
+    const I r = grid % kNumXcd;
+    const I x = pid % kNumXcd;
+    const I start = x * q + (x < r ? x : r);
     return start + pid / kNumXcd;
 }
 
@@ -44,18 +48,22 @@ struct TileCoord {
     int64_t n_block;
 };
 
-GEMM_HD TileCoord tile_coord(int64_t pid, int64_t num_m, int64_t num_n, int32_t swizzle, bool xcd) {
-    const int64_t grid = num_m * num_n;
-    const int64_t logical = xcd ? xcd_remap(pid, grid) : pid;
-    const int64_t per_group = num_m * swizzle;
-    const int64_t group = logical / per_group;
-    const int64_t first_n = group * swizzle;
-    const int64_t rest = num_n - first_n;
-    const int64_t width = rest < swizzle ? rest : swizzle;
-    const int64_t within = logical - group * per_group;
+template <class I>
+GEMM_HD TileCoord tile_coord(I pid, I num_m, I num_n, I swizzle, bool xcd) {
+    const I grid = num_m * num_n;
+    const I logical = xcd ? xcd_remap<I>(pid, grid) : pid;
+    // a group wider than the grid is the grid (same map), and keeps
+    // num_m * swizzle within the grid's range
+    if (swizzle > num_n) swizzle = num_n;
+    const I per_group = num_m * swizzle;
+    const I group = logical / per_group;
+    const I first_n = group * swizzle;
+    const I rest = num_n - first_n;
+    const I width = rest < swizzle ? rest : swizzle;
+    const I within = logical - group * per_group;
     TileCoord t;
-    t.m_block = within / width;
-    t.n_block = first_n + within % width;
+    t.m_block = (int64_t)(within / width);
+    t.n_block = (int64_t)(first_n + within % width);
     return t;
 }
 

@@ -2,12 +2,17 @@
 
     python -m dense_fp16_gemm_f16_amd.profile_summary stats DIR [--kernel gemm_f16_nt_kernel]
     python -m dense_fp16_gemm_f16_amd.profile_summary window DIR --kernel NAME [--min-us X] --skip N --count K
+    python -m dense_fp16_gemm_f16_amd.profile_summary counters DIR --kernel NAME
     python -m dense_fp16_gemm_f16_amd.profile_summary traffic \\
         --gemm-fetch DIR --gemm-write DIR --copy-fetch DIR --copy-write DIR \\
         --copy-bytes N --workload NAME --out profiles/traffic_NAME.json
 
 `stats` reads <DIR>/*_kernel_stats.csv (rocprofv3 --kernel-trace --stats
---output-format csv).  `traffic` reads <DIR>/*_counter_collection.csv of
+--output-format csv); `window` the kernel trace's launches by position;
+`counters` the per-dispatch values of every counter in
+<DIR>/*_counter_collection.csv, with the MFMA-busy share when
+SQ_VALU_MFMA_BUSY_CYCLES and GRBM_GUI_ACTIVE are among them (busy cycles
+summed over the 1024 SIMDs, over GPU-busy cycles summed over the 8 XCDs).  `traffic` reads <DIR>/*_counter_collection.csv of
 --pmc FETCH_SIZE / --pmc WRITE_SIZE runs (values in KiB per dispatch), scales
 each by the ratio of a plain copy's known bytes to what the same counter
 reported for it, and writes HBM bytes per GEMM launch together with a hash
@@ -80,6 +85,17 @@ def counter_per_dispatch(d: str, kernel: str, counter: str) -> list[float]:
     return [per[k] for k in sorted(per)]
 
 
+def counters(d: str, kernel: str) -> dict:
+    """Every counter of a --pmc run, per dispatch of `kernel`."""
+    path = _one(os.path.join(d, "**", "*counter_collection.csv"))
+    names = sorted({r["Counter_Name"] for r in csv.DictReader(open(path)) if kernel in r["Kernel_Name"]})
+    out = {c: counter_per_dispatch(d, kernel, c) for c in names}
+    if "SQ_VALU_MFMA_BUSY_CYCLES" in out and "GRBM_GUI_ACTIVE" in out:
+        out["mfma_busy_share"] = [round(b / 1024.0 / (g / 8.0), 4) for b, g in
+                                  zip(out["SQ_VALU_MFMA_BUSY_CYCLES"], out["GRBM_GUI_ACTIVE"])]
+    return out
+
+
 def main(argv=None) -> int:
     ap = argparse.ArgumentParser()
     sub = ap.add_subparsers(dest="cmd", required=True)
@@ -92,6 +108,9 @@ def main(argv=None) -> int:
     s3.add_argument("--min-us", type=float, default=0.0, help="only launches at least this long")
     s3.add_argument("--skip", type=int, default=0, help="matching launches to skip first")
     s3.add_argument("--count", type=int, required=True, help="matching launches to take after them")
+    s4 = sub.add_parser("counters", help="per-dispatch counter values of a --pmc run")
+    s4.add_argument("dir")
+    s4.add_argument("--kernel", default="gemm_f16")
     s2 = sub.add_parser("traffic")
     for k in ("gemm-fetch", "gemm-write", "copy-fetch", "copy-write", "workload", "out"):
         s2.add_argument("--" + k, required=True)
@@ -105,6 +124,9 @@ def main(argv=None) -> int:
         return 0
     if a.cmd == "window":
         print(json.dumps(kernel_window(a.dir, a.kernel, a.min_us, a.skip, a.count)))
+        return 0
+    if a.cmd == "counters":
+        print(json.dumps(counters(a.dir, a.kernel)))
         return 0
     fetch = counter_per_dispatch(a.gemm_fetch, a.kernel, "FETCH_SIZE")
     write = counter_per_dispatch(a.gemm_write, a.kernel, "WRITE_SIZE")

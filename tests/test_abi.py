@@ -89,6 +89,21 @@ def test_tile_coord_matches_the_oracle(nm, nn, sw, xcd):
     assert len(seen) == grid
 
 
+@pytest.mark.parametrize("nm,nn", [(46341, 46341), (65536, 65536), (3, 2**30 + 7), (2**31 - 1, 1), (2**31, 1)])
+@pytest.mark.parametrize("xcd", [0, 1])
+def test_tile_coord_at_the_32_bit_boundary(nm, nn, xcd):
+    """Grids below 2^31 tiles run the kernels' 32-bit arithmetic, larger ones
+    (which the GEMM entry points refuse) the 64-bit one; both match the
+    oracle at the ends of the grid and in between."""
+    grid = nm * nn
+    for sw in (1, 4, 7):
+        for pid in sorted({0, 1, 7, 8, grid // 3, grid // 2 + 5, grid - 9, grid - 8, grid - 1}):
+            if not 0 <= pid < grid:
+                continue
+            logical = raster.xcd_remap(pid, grid, 8) if xcd else pid
+            assert g.tile_coord(pid, nm, nn, sw, xcd) == raster.swizzle_tile_coord(logical, nm, nn, sw)
+
+
 def test_tile_coord_rejects_bad_input():
     for args in [(-1, 4, 4, 1, 0), (16, 4, 4, 1, 0), (0, 4, 4, 0, 0), (0, 0, 4, 1, 0)]:
         with pytest.raises(g.GemmError):
