@@ -25,6 +25,8 @@ LIB = os.path.join(HERE, "libgemm_f16.so")
 OBJ_DIR = os.path.join(HERE, "_build")
 TRACE_LIB = os.path.join(HERE, "libgemm_f16_trace.so")
 TRACE_OBJ_DIR = os.path.join(HERE, "_build_trace")
+TRACE_KT_LIB = os.path.join(HERE, "libgemm_f16_trace_kt.so")
+TRACE_KT_OBJ_DIR = os.path.join(HERE, "_build_trace_kt")
 CEILING_SRC = os.path.join(CSRC, "mfma_ceiling.hip")
 CEILING_LIB = os.path.join(HERE, "libmfma_ceiling.so")
 
@@ -77,8 +79,11 @@ def build(verbose: bool = False, extra: list[str] | None = None, jobs: int | Non
     return _build_lib(LIB, OBJ_DIR, list(extra or []), verbose, jobs)
 
 
-def build_trace(verbose: bool = False, jobs: int | None = None) -> str:
-    """The timestamp-traced copy of the library (measurement tool)."""
+def build_trace(verbose: bool = False, jobs: int | None = None, ktiles: bool = False) -> str:
+    """The timestamp-traced copy of the library (measurement tool); ktiles:
+    the copy that also stamps the K-tiles around the first tile change."""
+    if ktiles:
+        return _build_lib(TRACE_KT_LIB, TRACE_KT_OBJ_DIR, ["-DGEMM_F16_TRACE", "-DGEMM_F16_TRACE_KTILES"], verbose, jobs)
     return _build_lib(TRACE_LIB, TRACE_OBJ_DIR, ["-DGEMM_F16_TRACE"], verbose, jobs)
 
 
@@ -92,6 +97,6 @@ def build_ceiling(verbose: bool = False) -> str:
 
 if __name__ == "__main__":
     if "--trace" in sys.argv[1:]:
-        print(build_trace(verbose=True))
+        print(build_trace(verbose=True, ktiles="--ktiles" in sys.argv[1:]))
     else:
         print(build(verbose=True))

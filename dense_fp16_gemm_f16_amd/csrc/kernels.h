@@ -164,18 +164,27 @@ constexpr uint32_t kOutOfRange = 0x80000000u;  // buffer offset past any num_rec
 // the shader-clock counter (s_memtime) at their start, after the prologue's
 // wait, after the K loop and after their last store has completed, the
 // 100 MHz counter (s_memrealtime) at start and end, the cycles spent in the
-// release and acquire barriers of the K loop, the start of each of the
-// first six tiles (stream kernel), and the XCC and HW_ID registers.  Slots
-// of 20 words per wave, wave w of workgroup b at (4 b + w) * 20; workgroups
-// past kTraceBlocks and waves past the fourth record nothing.
+// release and acquire barriers of the K loop, and the XCC and HW_ID
+// registers; the stream kernel also the start of each of its first four
+// tiles and, with -DGEMM_F16_TRACE_KTILES as well, of K-tiles kt-1 of its
+// first tile and 0, 1 and 2 of its second (the first tile change; the low
+// 32 bits of the counter; these take scalar registers that the K loop
+// then spills to vector lanes).
+// Slots of 24 words per wave, wave w of workgroup b at (4 b + w) * 24;
+// workgroups past kTraceBlocks and waves past the fourth record nothing.
 #ifdef GEMM_F16_TRACE
-constexpr int kTraceBlocks = 2048, kTraceWords = 20;
+constexpr int kTraceBlocks = 2048, kTraceWords = 24;
 static __device__ unsigned long long gemm_trace[kTraceBlocks * 4 * kTraceWords];
 __device__ __forceinline__ uint64_t trace_clock() { return __builtin_amdgcn_s_memtime(); }
 __device__ __forceinline__ uint64_t trace_realtime() { return __builtin_amdgcn_s_memrealtime(); }
 struct TraceRecord {
     uint64_t t0 = 0, t1 = 0, rel = 0, acq = 0, acq_first = 0, tl = 0, r0 = 0, tiles = 0;
-    uint64_t tile_start[6] = {0, 0, 0, 0, 0, 0};
+    uint64_t tile_start[4] = {0, 0, 0, 0};
+#ifdef GEMM_F16_TRACE_KTILES
+    // around the first tile change: the counter's low 32 bits (differences
+    // of these are exact modulo 2^32)
+    uint32_t kt_last = 0, kt0 = 0, kt1 = 0, kt2 = 0;
+#endif
 };
 __device__ __forceinline__ void trace_write(const TraceRecord &r, int wave, int lane) {
     const uint64_t te = trace_clock(), re = trace_realtime();
@@ -192,9 +201,21 @@ __device__ __forceinline__ void trace_write(const TraceRecord &r, int wave, int 
     q[8] = re;
     q[9] = r.tiles;
 #pragma unroll
-    for (int i = 0; i < 6; ++i) q[10 + i] = r.tile_start[i];
+    for (int i = 0; i < 4; ++i) q[10 + i] = r.tile_start[i];
+    q[14] = 0;
+    q[15] = 0;
     q[16] = (unsigned)__builtin_amdgcn_s_getreg(20 | (3 << 11));  // XCC_ID[3:0]
     q[17] = (unsigned)__builtin_amdgcn_s_getreg(4 | (31 << 11));  // HW_ID
+    q[18] = 0;
+    q[19] = 0;
+#ifdef GEMM_F16_TRACE_KTILES
+    q[20] = r.kt_last;
+    q[21] = r.kt0;
+    q[22] = r.kt1;
+    q[23] = r.kt2;
+#else
+    q[20] = q[21] = q[22] = q[23] = 0;
+#endif
 }
 #define GEMM_TRACE_DO(...) __VA_ARGS__
 #else
@@ -2015,6 +2036,16 @@ void gemm_f16_stream_kernel(const Params p) {
         constexpr int S = decltype(s_c)::value;
         constexpr bool FIRST = decltype(first_c)::value;
         constexpr int SN = S ^ 1;
+#if defined(GEMM_F16_TRACE) && defined(GEMM_F16_TRACE_KTILES)
+        if (tr.tiles == 1) {
+            if (t == kt_count - 1) tr.kt_last = (uint32_t)trace_clock();
+        } else if (tr.tiles == 2 && t < 3) {
+            const uint32_t tk = (uint32_t)trace_clock();
+            if (t == 0) tr.kt0 = tk;
+            else if (t == 1) tr.kt1 = tk;
+            else tr.kt2 = tk;
+        }
+#endif
         opa.refresh_lds();
         opb.refresh_lds();
         constexpr int B1 = S == 0 ? 1 : 2;   // this K-tile's step-1 buffer
@@ -2096,7 +2127,7 @@ void gemm_f16_stream_kernel(const Params p) {
         {
             const uint64_t ts = trace_clock();
 #pragma unroll
-            for (int i = 0; i < 6; ++i)
+            for (int i = 0; i < 4; ++i)
                 if (tr.tiles == (uint64_t)i) tr.tile_start[i] = ts;  // constant indexes: no scratch
             ++tr.tiles;
         }

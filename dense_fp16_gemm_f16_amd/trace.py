@@ -1,15 +1,19 @@
 """Per-wave timestamps of the 256x256 kernels from the traced build of the library.
 
-    python -m dense_fp16_gemm_f16_amd.trace [--workloads NAME ...] [--shapes M,N,K ...]
-                                            [--launches 30] [--repeat 2] [--save DIR] [--build]
+    python -m dense_fp16_gemm_f16_amd.trace [--workloads NAME ...] [--shapes M,N,K ...] [--dist D]
+                                            [--launches 30] [--repeat 2] [--save DIR] [--build] [--ktiles]
 
 libgemm_f16_trace.so is the library compiled with -DGEMM_F16_TRACE
 (build.build_trace(); --build rebuilds it).  Its fragment-ahead and stream
 kernels record, per wave, the shader-clock counter at their start, after the
 prologue's wait, after the K loop and after their last store, the 100 MHz
 counter at start and end, the cycles spent waiting in the K loop's two
-barriers, the start of each tile (stream kernel, first six) and the XCC the
-wave ran on.  Each run launches the GEMM on the 256x256 tile `--launches`
+barriers and the XCC the wave ran on; the stream kernel also the start of
+each of its first four tiles.  --ktiles uses libgemm_f16_trace_kt.so, which
+also stamps the K-tiles around the stream kernel's first tile change (the
+last of the first tile, the first three of the second); those stamps cost
+its K loop some scalar-register spills, so the other figures come from the
+plain traced build.  Each run launches the GEMM on the 256x256 tile `--launches`
 times back to back (the device settles at its loaded clock) and reads the
 last launch's words.
 
@@ -35,7 +39,7 @@ import dense_fp16_gemm_f16_amd as _g
 from dense_fp16_gemm_f16_amd import build as _build
 
 TRACE_BLOCKS = 2048
-TRACE_WORDS = 20
+TRACE_WORDS = 24
 MFMA_CYCLES_PER_KTILE = 128 * 16  # per wave: 8 x 8 blocks x 2 k steps, 16 cycles each
 BK = 64
 
@@ -82,10 +86,18 @@ def summarize(words: np.ndarray, k: int) -> dict:
         "clock_ghz": q(clock),
         "xcc": {},
     }
-    if tiles.max() > 1:
-        s = w[:, 10:16]
-        n = int(min(tiles.min(), 6))
+    if tiles.min() > 1:
+        s = w[:, 10:14]
+        n = int(min(tiles.min(), 4))
         rec["tile_cycles"] = [q(s[:, i + 1] - s[:, i]) for i in range(n - 1)]
+        if kt >= 4 and (w[:, 20] != 0).all():
+            kl, k0, k1, k2 = (w[:, 20 + i] for i in range(4))
+            m32 = 1 << 32  # the stamps are the counter's low 32 bits
+            rec["first_tile_change_cycles"] = {
+                "last_ktile_of_tile_1_and_change": q((k0 - kl) % m32),
+                "ktile_0_of_tile_2": q((k1 - k0) % m32),
+                "ktile_1_of_tile_2": q((k2 - k1) % m32),
+            }
     for x in sorted(set(xcc.tolist())):
         sel = xcc == x
         rec["xcc"][str(x)] = {"waves": int(sel.sum()), "clock_ghz": round(float(np.median(clock[sel])), 4),
@@ -97,10 +109,11 @@ def summarize(words: np.ndarray, k: int) -> dict:
     return rec
 
 
-def load(rebuild: bool = False) -> ctypes.CDLL:
-    if rebuild or not os.path.exists(_build.TRACE_LIB):
-        _build.build_trace()
-    lib = ctypes.CDLL(_build.TRACE_LIB)
+def load(rebuild: bool = False, ktiles: bool = False) -> ctypes.CDLL:
+    path = _build.TRACE_KT_LIB if ktiles else _build.TRACE_LIB
+    if rebuild or not os.path.exists(path):
+        _build.build_trace(ktiles=ktiles)
+    lib = ctypes.CDLL(path)
     i64, vp = ctypes.c_int64, ctypes.c_void_p
     lib.gemm_f16_nt_ex.argtypes = [i64, i64, i64, vp, vp, vp, vp, ctypes.POINTER(_g.Options)]
     lib.gemm_f16_nt_ex.restype = ctypes.c_int
@@ -140,14 +153,16 @@ def main(argv=None) -> int:
     ap.add_argument("--launches", type=int, default=30)
     ap.add_argument("--repeat", type=int, default=2)
     ap.add_argument("--save", default=None, help="directory for the raw words (.npy)")
-    ap.add_argument("--build", action="store_true", help="rebuild libgemm_f16_trace.so first")
+    ap.add_argument("--build", action="store_true", help="rebuild the traced library first")
+    ap.add_argument("--ktiles", action="store_true",
+                    help="the build that also stamps the K-tiles around the first tile change")
     a = ap.parse_args(argv)
 
     import torch
 
     from dense_fp16_gemm_f16_amd import inputs
 
-    lib = load(a.build)
+    lib = load(a.build, a.ktiles)
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream(dev).cuda_stream
     cases = []

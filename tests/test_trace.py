@@ -18,6 +18,8 @@ def _words(waves):
         for j, v in enumerate(d.get("tile_start", [])):
             row[10 + j] = v
         row[16] = d.get("xcc", 0)
+        for j, v in enumerate(d.get("kt_stamps", [])):
+            row[20 + j] = v
     return w
 
 
@@ -34,7 +36,9 @@ def test_summary_of_a_made_up_trace():
             waves.append(dict(t0=t0, t1=t0 + 4_000, tl=t0 + 4_000 + 80_000, te=t0 + cycles,
                               rel=32 * 50, acq=32 * 25, acq_first=2 * 300, tiles=2,
                               r0=500 + wg, re=500 + wg + ticks, xcc=wg,
-                              tile_start=[t0 + 4_000, t0 + 44_000]))
+                              tile_start=[t0 + 4_000, t0 + 44_000],
+                              # low 32 bits, wrapping between the second and third
+                              kt_stamps=[2**32 - 5_500, 2**32 - 3_000, 0, 2_500]))
     s = trace.summarize(_words(waves), 1024)
     assert s["waves"] == 8
     assert s["k_tiles_per_tile"] == 16
@@ -48,6 +52,10 @@ def test_summary_of_a_made_up_trace():
     assert s["barrier_wait_cycles_per_ktile"]["acquire"]["median"] == 25
     assert s["acquire_wait_first_ktile_of_tile_cycles"]["median"] == 300
     assert s["tile_cycles"][0]["median"] == 40_000
+    change = s["first_tile_change_cycles"]
+    assert change["last_ktile_of_tile_1_and_change"]["median"] == 2_500
+    assert change["ktile_0_of_tile_2"]["median"] == 3_000
+    assert change["ktile_1_of_tile_2"]["median"] == 2_500
     assert s["xcc"]["0"]["clock_ghz"] == pytest.approx(2.0, rel=1e-3)
     assert s["xcc"]["1"]["clock_ghz"] == pytest.approx(1.0, rel=1e-3)
     # XCC 1 starts one tick later and runs twice as long
