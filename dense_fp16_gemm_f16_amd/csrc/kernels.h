@@ -1,4 +1,6 @@
-// libgemm_f16: C = fp16(A * B^T), fp16 inputs, fp32 accumulation, for gfx950.
+// libgemm_f16: C = fp16(A * B^T), fp16 inputs, fp32 accumulation, for gfx950:
+// the device code and the per-tile launch logic (instantiated per block tile
+// in tile_*.hip and ring_*.hip).
 //
 // The operation is the one the Tilus tutorial "1. WGMMA: Hopper's
 // Asynchronous Tensor Core" builds in "The Full Kernel": A is [M,K], B is
@@ -6,37 +8,37 @@
 // block_k steps, and the accumulator is cast to fp16 and stored at the
 // block's (m, n) offset.  The mechanism here is CDNA4's, not Hopper's:
 //
-//  * scheduler  one workgroup per output block tile over a 1D grid,
-//               XCD-aware and swizzle-rasterized (tile_sched.h);
-//  * loader     buffer_load_dwordx4 of 16-byte K-chunks (one 128-byte row
-//               segment per 8 lanes), staged in VGPRs one K-tile ahead and
-//               written to a 2-stage LDS ring.  Buffer descriptors bound
-//               each operand tile, so rows past M / N read as zero; when K
-//               is a multiple of the K-tile one descriptor serves the whole
-//               K walk and the K-tile offset rides in the scalar offset.
-//               For C = A B^T with K a multiple of 8 and 16-byte aligned
-//               operands the loads go straight into LDS instead
-//               (gemm_f16_direct_kernel: no staging registers, no LDS
-//               write instructions);
-//  * LDS        a stage holds each operand as four 16-wide k planes of
-//               32-byte rows; within a row the two 16-byte halves swap by
-//               a bit of the row index and planes are padded, so both the
-//               MFMA fragment reads and the loader's writes are free of
-//               bank conflicts, and every LDS address is one per-lane base
-//               register plus an immediate offset (the direct path: 128-byte
-//               rows with 16-byte chunks swizzled by the row index);
-//  * compute    WM x WN waves (4 or 8), each owning a (BM/WM) x (BN/WN) piece of C
-//               as independent 32x32 fp32 accumulators fed by
-//               v_mfma_f32_32x32x16_f16; fragment reads run one 16-wide k
-//               step ahead of the MFMAs that use them;
+//  * scheduler  a 1D grid, XCD-aware and swizzle-rasterized (tile_sched.h):
+//               one workgroup per block tile, or, with more tiles than
+//               CUs, one per CU walking tiles blockIdx.x, + gridDim.x, ...
+//  * loader     for C = A B^T with K % 8 == 0 and 16-byte aligned operands,
+//               buffer_load_dwordx4 ... lds straight into a 2-stage LDS ring
+//               (KMajorDirect: 1 KB = 8 rows of 128 bytes per wave
+//               instruction; lanes past K get an out-of-range offset and
+//               land as zeros).  Otherwise 16/8/4/2-byte loads staged in
+//               VGPRs one K-tile ahead (KMajorOperand).  Buffer descriptors
+//               bound each operand tile, so rows past M / N read as zero;
+//  * LDS        direct path: 128-byte rows with the 16-byte chunks
+//               swizzled by the row index, conflict-free fragment reads;
+//               register-staged path: four 16-wide k planes of 32-byte
+//               rows.  Every LDS address is one per-lane base register plus
+//               an immediate offset;
+//  * compute    4 waves in a 2 x 2 grid (8 on one tile), each owning a
+//               (BM/WM) x (BN/WN) piece of C: v_mfma_f32_16x16x32_f16 with
+//               the accumulators tied in AGPRs (inline asm) on the direct
+//               path, v_mfma_f32_32x32x16_f16 on the register-staged one.
+//               The fragments of K-tile t+1 are read during K-tile t
+//               (gemm_f16_direct_ahead_kernel), behind a release and an
+//               acquire barrier per K-tile;
 //  * epilogue   fp32 -> fp16 round-to-nearest-even (or the fp32 value
-//               itself), each wave's piece of C staged through LDS so that
-//               16 consecutive lanes store one contiguous row segment;
-//               stores masked to [M, N].
+//               itself), masked to [M, N]: staged through LDS so that 16
+//               consecutive lanes store one contiguous row segment, or, in
+//               gemm_f16_stream_kernel, stored straight from the
+//               accumulators under the next tile's first MFMAs.
 //
 // The sum of each output runs over K-tiles in increasing order, and inside
-// a K-tile over 16-wide k steps in increasing order, whatever the grid
-// order: results do not depend on the rasterization options.
+// a K-tile over its k steps in increasing order, whatever the grid order:
+// results do not depend on the rasterization options.
 #pragma once
 
 #include <hip/hip_runtime.h>

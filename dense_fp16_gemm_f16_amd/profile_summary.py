@@ -27,21 +27,34 @@ import glob
 import hashlib
 import json
 import os
+import re
 import statistics
 import sys
 
 CSRC = os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc")
 
 
+_COMMENT = re.compile(r"//[^\n]*|/\*.*?\*/", re.S)
+
+
+def code_text(src: str) -> str:
+    """The source with its comments removed and each run of white space made
+    one blank: edits to comments or layout leave it unchanged.  (The sources
+    hashed here have no string or character literal that holds // or /*.)"""
+    return " ".join(_COMMENT.sub(" ", src).split())
+
+
 def kernel_source_hash() -> str:
-    """Hash of every source the library's kernels are built from (the host
-    side, the kernel templates, the scheduler and the per-tile units)."""
+    """Hash of the code of every source the library is built from (the host
+    side, the kernel templates, the scheduler and the per-tile units),
+    comments and layout aside."""
     h = hashlib.sha256()
     names = ["gemm_f16.hip", "kernels.h", "tile_sched.h"] + sorted(
         os.path.basename(p) for p in glob.glob(os.path.join(CSRC, "tile_*.hip")) + glob.glob(os.path.join(CSRC, "ring_*.hip")))
     for name in names:
-        with open(os.path.join(CSRC, name), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(CSRC, name), encoding="utf-8") as f:
+            h.update(name.encode())
+            h.update(code_text(f.read()).encode())
     return h.hexdigest()[:16]
 
 
