@@ -6,8 +6,11 @@ own, all in parallel, then linked into one shared library.
 
 build_ceiling() builds the MFMA-rate probe libmfma_ceiling.so, and
 build_trace() the timestamp-traced copy of the library, libgemm_f16_trace.so
-(the same sources with -DGEMM_F16_TRACE): measurement tools that are not part
-of the library (tune.py --ceiling and trace.py build them on demand).
+(the same sources with -DGEMM_F16_TRACE), and build_poison() the debug copy
+whose kernels fill their LDS with NaN before the first load,
+libgemm_f16_poison.so (-DGEMM_F16_POISON_LDS): measurement and debug tools
+that are not part of the library (tune.py --ceiling, trace.py and the tests
+use them).
 """
 from __future__ import annotations
 
@@ -27,6 +30,8 @@ TRACE_LIB = os.path.join(HERE, "libgemm_f16_trace.so")
 TRACE_OBJ_DIR = os.path.join(HERE, "_build_trace")
 TRACE_KT_LIB = os.path.join(HERE, "libgemm_f16_trace_kt.so")
 TRACE_KT_OBJ_DIR = os.path.join(HERE, "_build_trace_kt")
+POISON_LIB = os.path.join(HERE, "libgemm_f16_poison.so")
+POISON_OBJ_DIR = os.path.join(HERE, "_build_poison")
 CEILING_SRC = os.path.join(CSRC, "mfma_ceiling.hip")
 CEILING_LIB = os.path.join(HERE, "libmfma_ceiling.so")
 
@@ -95,8 +100,15 @@ def build_ceiling(verbose: bool = False) -> str:
     return CEILING_LIB
 
 
+def build_poison(verbose: bool = False, jobs: int | None = None) -> str:
+    """The debug copy of the library whose kernels poison their LDS with NaN."""
+    return _build_lib(POISON_LIB, POISON_OBJ_DIR, ["-DGEMM_F16_POISON_LDS"], verbose, jobs)
+
+
 if __name__ == "__main__":
     if "--trace" in sys.argv[1:]:
         print(build_trace(verbose=True, ktiles="--ktiles" in sys.argv[1:]))
+    elif "--poison" in sys.argv[1:]:
+        print(build_poison(verbose=True))
     else:
         print(build(verbose=True))

@@ -160,6 +160,24 @@ constexpr uint32_t kOutOfRange = 0x80000000u;  // buffer offset past any num_rec
 #define GEMM_STAGE_SETS 1
 #endif
 
+// LDS poisoning (built only with -DGEMM_F16_POISON_LDS, a debug build of
+// the library, never the library itself): every kernel fills its LDS with
+// fp16 NaN (0x7E00) before its first load, and waits for it, so an MFMA
+// operand read from LDS that no load (or zero-filling out-of-range load)
+// has written turns its outputs into NaN, which the parity tests catch.
+#ifdef GEMM_F16_POISON_LDS
+__device__ __forceinline__ void poison_lds(char *smem, int bytes) {
+    typedef int int4p __attribute__((ext_vector_type(4)));
+    const int4p nan = {0x7E007E00, 0x7E007E00, 0x7E007E00, 0x7E007E00};
+    for (int o = (int)threadIdx.x * 16; o < bytes; o += (int)blockDim.x * 16)
+        *reinterpret_cast<int4p *>(smem + o) = nan;
+    __syncthreads();
+}
+#define GEMM_POISON_LDS(smem) poison_lds(smem, (int)sizeof(smem))
+#else
+#define GEMM_POISON_LDS(smem)
+#endif
+
 // Timestamp trace (built only with -DGEMM_F16_TRACE, a profiling build of
 // the library, never the library itself): the fragment-ahead and stream
 // kernels record per wave, in this translation unit's copy of gemm_trace,
@@ -728,6 +746,7 @@ void gemm_f16_kernel(const Params p) {
     constexpr int kLdsB = OpA::kLdsBytes;
     static_assert(OpA::kLdsBytes + OpB::kLdsBytes <= 160 * 1024, "LDS budget");
     __shared__ __attribute__((aligned(1024))) char smem[OpA::kLdsBytes + OpB::kLdsBytes];
+    GEMM_POISON_LDS(smem);
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
@@ -1181,6 +1200,7 @@ void gemm_f16_direct_kernel(const Params p) {
     static_assert(OpA::kStage + (FM - 1) * C::MB * 128 < 65536 && OpB::kStage + (FN - 1) * C::MB * 128 < 65536,
                   "LDS immediates must fit the 16-bit offset field");
     __shared__ __attribute__((aligned(1024))) char smem[kLds];
+    GEMM_POISON_LDS(smem);
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
@@ -1375,6 +1395,7 @@ void gemm_f16_direct_ahead_kernel(const Params p) {
                       OpB::kStage + 36 * (BN * 2) < 65536,
                   "LDS immediates must fit the 16-bit offset field");
     __shared__ __attribute__((aligned(1024))) char smem[kLds];
+    GEMM_POISON_LDS(smem);
 
     GEMM_TRACE_DO(TraceRecord tr; tr.t0 = trace_clock(); tr.r0 = trace_realtime(); tr.tiles = 1;)
     const int tid = threadIdx.x;
@@ -1562,6 +1583,7 @@ void gemm_f16_persistent_kernel(const Params p) {
                       OpB::kStage + 36 * (BN * 2) < 65536,
                   "LDS immediates must fit the 16-bit offset field");
     __shared__ __attribute__((aligned(1024))) char smem[kLds + kSpare];
+    GEMM_POISON_LDS(smem);
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);
@@ -1875,6 +1897,7 @@ void gemm_f16_stream_kernel(const Params p) {
     static_assert(OpA::kStage + (FM - 1) * C::MB * 128 < 65536 && OpB::kStage + (FN / 2 - 1) * 32 * 128 < 65536,
                   "LDS immediates must fit the 16-bit offset field");
     __shared__ __attribute__((aligned(1024))) char smem[kLds];
+    GEMM_POISON_LDS(smem);
 
     GEMM_TRACE_DO(TraceRecord tr; tr.t0 = trace_clock(); tr.r0 = trace_realtime();)
     const int tid = threadIdx.x;
@@ -2270,6 +2293,7 @@ void gemm_f16_ring_kernel(const Params p) {
     // (a stage offset past the 16-bit LDS immediate costs the compiler an
     // address add per read; deep rings of large stages pay it)
     __shared__ __attribute__((aligned(1024))) char smem[kLds];
+    GEMM_POISON_LDS(smem);
 
     const int tid = threadIdx.x;
     const int lane = tid & (kWave - 1);

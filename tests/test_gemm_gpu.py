@@ -488,6 +488,35 @@ def test_variants_bit_exact(tile, variant):
                           f"variant {variant} tile {tile} {m}x{n}x{k}")
 
 
+# Race check.  Every 4-wave tile's direct-to-LDS kernels, the
+# one-workgroup-per-CU kernels and every kernel variant run
+# v_mfma_f32_16x16x32_f16 over K in 32-wide k steps in increasing order, so
+# each output's fp32 sum is formed in the same order whatever the kernel,
+# tile, ring depth or loader arrangement: on random operands their C must
+# agree bit for bit.  A race (a stale or early LDS read, a stage reused too
+# soon) shows up as a difference.  Shapes: one tile per workgroup (and the
+# K tail), the stream kernel (more 256x256 tiles than CUs) and the
+# persistent one (64x64, 64x128, 128x64 tiles).
+M16_DIRECT_TILES = [g.TILE_256x256, g.TILE_256x128, g.TILE_128x256, g.TILE_128x128, g.TILE_128x128_M16,
+                    g.TILE_64x64, g.TILE_64x128, g.TILE_128x64]
+
+
+@pytest.mark.parametrize("m,n,k", [(1000, 1100, 640), (1000, 1100, 1000), (4608, 4096, 256), (2100, 2112, 1024)])
+def test_same_bits_across_kernels(m, n, k):
+    _announce("same bits", m, n, k)
+    rng = np.random.default_rng(m * 7 + n * 3 + k)
+    a = rng.standard_normal((m, k)).astype(np.float16)
+    b = rng.standard_normal((n, k)).astype(np.float16)
+    base = run_gemm(a, b, tile=g.TILE_256x256)
+    assert_ulp(base, oracle.gemm_f16_nt(a, b), k, f"{m}x{n}x{k} 256x256")
+    for tile in M16_DIRECT_TILES:
+        assert_bits_equal(run_gemm(a, b, tile=tile), base, f"{m}x{n}x{k} tile {tile}")
+    for tile, variants in VARIANT_TILES.items():
+        for v in variants:
+            if k % g.VARIANTS[v][0] == 0:
+                assert_bits_equal(run_gemm(a, b, tile=tile, variant=v), base, f"{m}x{n}x{k} tile {tile} variant {v}")
+
+
 @pytest.mark.parametrize("variant", [1, 4, 6])
 def test_variants_random_operands(variant):
     """uniform[-1,1] operands, 1024x1024x2048 on the 128x128 tile: ulp bar."""
