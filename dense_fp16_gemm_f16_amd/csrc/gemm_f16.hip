@@ -245,6 +245,7 @@ static int gemm_impl(bool nn, int64_t m, int64_t n, int64_t k, const void *a, co
     p.k_tiles = (int32_t)cdiv(k, 64);
     p.swizzle = o.swizzle ? o.swizzle : 4;
     p.xcd = o.xcd < 0 ? 1 : o.xcd;
+    p.c_lines = !nn && (n * 2) % 128 == 0 && ((uintptr_t)c % 128) == 0;
     if ((int64_t)p.num_m * p.num_n >= (int64_t(1) << 31)) return GEMM_F16_EINVAL;
 
     hipError_t e;

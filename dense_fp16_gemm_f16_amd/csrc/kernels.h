@@ -251,6 +251,7 @@ struct Params {
     int32_t k_tiles;       // ceil(k / BK)
     int32_t swizzle;
     int32_t xcd;
+    int32_t c_lines;       // fp16 C whose rows are whole 128-byte lines (N % 64 == 0, C 128-byte aligned)
 };
 
 // Block-tile configuration: BM x BN output tile, K walked 64 at a time in
@@ -631,7 +632,13 @@ struct CStaging {
         if (m < p.m && n < p.n) {
             Out *crow = static_cast<Out *>(p.c) + (int64_t)m * p.n;
             if (vec16 && n + 16 / ES - 1 < p.n) {
-                *reinterpret_cast<int4v *>(crow + n) = v;
+                // streaming (non-temporal) where C's rows are whole lines:
+                // the C lines then do not displace A and B lines in L2
+                // (rows that end inside a line measured slower with it)
+                if (!NN && p.c_lines)
+                    __builtin_nontemporal_store(v, reinterpret_cast<int4v *>(crow + n));
+                else
+                    *reinterpret_cast<int4v *>(crow + n) = v;
             } else {
                 union {
                     int4v v;
@@ -2493,7 +2500,7 @@ hipError_t launch(const Params &p, int g, int cus, hipStream_t stream) {
                     p.n % 8 == 0 && ((uintptr_t)p.c % 16) == 0 && (int64_t)CD::BM * p.n * 2 < (int64_t(1) << 31)) {
                     if constexpr (GEMM_STREAM && CD::FM * CD::FN >= 16) {
                         // rows of C that are whole 128-byte lines: streaming stores
-                        const bool lines = GEMM_STREAM_NT && (p.n * 2) % 128 == 0 && ((uintptr_t)p.c % 128) == 0;
+                        const bool lines = GEMM_STREAM_NT && p.c_lines;
                         return lines ? launch_kernel(gemm_f16_stream_kernel<CD, true>, dim3((unsigned)cus), block,
                                                      stream, p)
                                      : launch_kernel(gemm_f16_stream_kernel<CD, false>, dim3((unsigned)cus), block,
