@@ -59,9 +59,13 @@ def kernel_source_hash() -> str:
 
 
 def _one(pattern: str) -> str:
+    """The one file matching `pattern`; a folder that holds several runs is
+    ambiguous and raises rather than reading whichever sorts first."""
     files = sorted(glob.glob(pattern, recursive=True))
     if not files:
         raise FileNotFoundError(pattern)
+    if len(files) > 1:
+        raise ValueError(f"{len(files)} files match {pattern}: {files[:4]}; give one run's folder")
     return files[0]
 
 

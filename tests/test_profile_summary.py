@@ -3,6 +3,8 @@ traffic to the kernel code, and the trace-window selection."""
 import csv
 import os
 
+import pytest
+
 from dense_fp16_gemm_f16_amd import profile_summary as ps
 
 
@@ -59,3 +61,10 @@ def test_window_picks_launches_by_position(tmp_path):
         w.writerows(rows)
     r = ps.kernel_window(str(tmp_path), "gemm_f16", 400, 1, 2)
     assert r["launches"] == 2 and r["min_us"] == 600 and r["max_us"] == 700
+
+
+def test_a_folder_with_two_runs_is_refused(tmp_path):
+    for pid in (1, 2):
+        (tmp_path / f"run_{pid}_kernel_trace.csv").write_text("Kernel_Name,Start_Timestamp,End_Timestamp\n")
+    with pytest.raises(ValueError, match="2 files match"):
+        ps.kernel_window(str(tmp_path), "gemm_f16", 0, 0, 1)
