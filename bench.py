@@ -15,8 +15,12 @@ warm-up launches, then 50 event-timed ones, 200 for the launch-bound
 exactly K timed GEMMs between two device synchronisations, every launch
 also bracketed by HIP events on the stream it runs on (the kernel's average
 duration, for the roofline figure); then a sustained run of back-to-back
-GEMMs for at least --sustain seconds, and a cold-cache figure (a 512 MiB
-buffer written before each launch).  `value` is the median over the
+GEMMs for at least --sustain seconds, a cold-cache figure (a 512 MiB
+buffer written before each launch), and last each other workload back to
+back for at least --config-sustain seconds ("sustained_tflops" in
+`configs`: the clock needs milliseconds to settle after the load changes,
+so the 50-launch figures of the shorter workloads catch it still moving).
+`value` is the median over the
 children of the headline's K-step wall-clock rate; the per-workload figures
 are medians too.  The headline thus runs on a device at its operating
 point; the first child also times the headline's first W + K steps on the
@@ -213,6 +217,24 @@ def child(args) -> int:
     out["cold_kernel_us"] = cold
     del flush
 
+    # every other workload sustained too: back-to-back launches for at least
+    # --config-sustain seconds each, after the headline's figures so that they
+    # do not change the state the headline runs in
+    if args.config_sustain > 0:
+        for name in order:
+            if name == args.workload:
+                continue
+            cw, cbufs, cstep = setups[name]
+            us = statistics.median(out["configs"][name]["kernel_us"])
+            n = max(1, int(args.config_sustain / (us * 1e-6)) + 1)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(n):
+                cstep()
+            torch.cuda.synchronize()
+            out["configs"][name]["sustained"] = {"launches": n, "seconds": time.perf_counter() - t0}
+        log(f"child {args.index}: other workloads sustained")
+
     # outputs for the parity check (first child), from a launch of its own
     if args.index == 0:
         for name in order:
@@ -319,6 +341,8 @@ def main() -> int:
     ap.add_argument("--procs", type=int, default=3, help="fresh processes timed (median reported)")
     ap.add_argument("--sustain", type=float, default=1.0,
                     help="seconds of back-to-back headline GEMMs per process (0 = skip)")
+    ap.add_argument("--config-sustain", type=float, default=1.0,
+                    help="seconds of back-to-back launches of each other workload (0: skip)")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle work for the CPU baseline (0 = skip it and the parity checks)")
     ap.add_argument("--traffic-calibration", type=int, default=0, metavar="BYTES",
@@ -371,7 +395,7 @@ def main() -> int:
             cmd = [sys.executable, os.path.abspath(__file__), "--child", tmp, "--index", str(i),
                    "--steps", str(args.steps), "--warmup", str(args.warmup), "--workload", args.workload,
                    "--tile", str(args.tile), "--swizzle", str(args.swizzle), "--xcd", str(args.xcd),
-                   "--sustain", str(args.sustain)]
+                   "--sustain", str(args.sustain), "--config-sustain", str(args.config_sustain)]
             rc = subprocess.run(cmd).returncode
             if rc != 0:
                 log(f"child {i} failed with status {rc}")
@@ -446,10 +470,17 @@ def main() -> int:
             per = [statistics.median(r["configs"][name]["kernel_us"]) for r in results]
             us = statistics.median(per)
             tf = cw.flops / (us * 1e-6) / 1e12
-            cfgs.append({"workload": name, "m": cw.m, "n": cw.n, "k": cw.k, "values": cw.dist,
-                         "tile": results[0]["configs"][name]["tile"], "kernel_median_us": round(us, 2),
-                         "tflops": round(tf, 1), "frac": round(tf / PEAK_TFLOPS, 4),
-                         "traffic": measured_traffic(name)})
+            cfg = {"workload": name, "m": cw.m, "n": cw.n, "k": cw.k, "values": cw.dist,
+                   "tile": results[0]["configs"][name]["tile"], "kernel_median_us": round(us, 2),
+                   "tflops": round(tf, 1), "frac": round(tf / PEAK_TFLOPS, 4),
+                   "traffic": measured_traffic(name)}
+            if name == w.name and "sustained" in rec:
+                cfg["sustained_tflops"] = rec["sustained"]["tflops"]
+            elif all("sustained" in r["configs"][name] for r in results):
+                cfg["sustained_tflops"] = round(statistics.median(
+                    cw.flops * r["configs"][name]["sustained"]["launches"]
+                    / r["configs"][name]["sustained"]["seconds"] / 1e12 for r in results), 1)
+            cfgs.append(cfg)
         rec["configs"] = cfgs
         if nn:
             rec["metric"] = "fp16 GEMM D = A*B (B [K,N], fp32 out) TFLOP/s; % of MI355X dense fp16 MFMA peak"
