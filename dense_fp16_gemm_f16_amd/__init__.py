@@ -53,6 +53,7 @@ EXPORTS = (
     "gemm_f16_status_string",
     "gemm_f16_tile_coord",
     "gemm_f16_select_tile",
+    "gemm_f16_select_xcd",
 )
 
 
@@ -96,6 +97,8 @@ def lib() -> ctypes.CDLL:
     L.gemm_f16_tile_coord.restype = ctypes.c_int
     L.gemm_f16_select_tile.argtypes = [i64, i64, i64]
     L.gemm_f16_select_tile.restype = ctypes.c_int
+    L.gemm_f16_select_xcd.argtypes = [i64, i64, i32, i32]
+    L.gemm_f16_select_xcd.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -195,6 +198,13 @@ def tile_coord(pid: int, num_m: int, num_n: int, swizzle: int, xcd: int) -> tupl
 
 def select_tile(m: int, n: int, k: int) -> int:
     rc = lib().gemm_f16_select_tile(m, n, k)
+    if rc < 0:
+        raise GemmError(rc)
+    return rc
+
+
+def select_xcd(num_m: int, num_n: int, swizzle: int = 4, cus: int = 256) -> int:
+    rc = lib().gemm_f16_select_xcd(num_m, num_n, swizzle, cus)
     if rc < 0:
         raise GemmError(rc)
     return rc

@@ -75,7 +75,8 @@ int gemm_f16_nt(int64_t m, int64_t n, int64_t k, const void *a, const void *b,
  *            "4. Pipeline Abstraction and Two Consumer Warp Groups", section
  *            "Tile Rasterization"); 0 = library default, 1 = plain grid.
  *   xcd      1 = give each of the 8 XCDs a contiguous run of tiles,
- *            0 = hardware dispatch order, -1 = library default.
+ *            0 = hardware dispatch order, -1 = library default
+ *            (gemm_f16_select_xcd).
  *   variant  0 = the library's kernels.  1..7 = a kernel whose K-tile width
  *            (block_k), LDS ring depth and wave roles are those of the
  *            GEMM_F16_VARIANT_* below, one tile per workgroup (the tuning
@@ -164,11 +165,23 @@ int gemm_f16_tile_coord(int64_t pid, int64_t num_m, int64_t num_n, int32_t swizz
                         int32_t xcd, int64_t *m_block, int64_t *n_block);
 
 /*
- * Block tile the automatic choice would use for (m, n, k): one of
- * GEMM_F16_TILE_*, or a negative status for invalid sizes.  Pure host
- * function: no HIP call.
+ * Block tile the automatic choice would use for (m, n, k) on the current
+ * device: one of GEMM_F16_TILE_*, or a negative status for invalid sizes.
+ * Asks HIP for the device's compute-unit count (once per device); with no
+ * device it assumes 256.
  */
 int gemm_f16_select_tile(int64_t m, int64_t n, int64_t k);
+
+/*
+ * The xcd option that xcd = -1 stands for, on a grid of num_m x num_n
+ * block tiles rasterized `swizzle` tile-columns wide, on a device of `cus`
+ * compute units: 1 (remap) except on a grid of exactly `cus` tiles whose
+ * dispatch order leaves no XCD more operand panels (distinct tile rows
+ * plus tile columns) than the remap does; then 0.  Returns
+ * GEMM_F16_EINVAL for num_m, num_n or swizzle below 1, cus below 0, or
+ * 2^31 tiles or more.  Pure host function: no HIP call.
+ */
+int gemm_f16_select_xcd(int64_t num_m, int64_t num_n, int32_t swizzle, int32_t cus);
 
 #ifdef __cplusplus
 }

@@ -123,6 +123,42 @@ def test_select_tile():
         g.select_tile(-1, 4, 4)
 
 
+def _busiest_xcd_panels(nm, nn, sw, remap):
+    grid = nm * nn
+    most = 0
+    for x in range(8):
+        rows, cols = set(), set()
+        for pid in range(x, grid, 8):
+            logical = raster.xcd_remap(pid, grid, 8) if remap else pid
+            mb, nb = raster.swizzle_tile_coord(logical, nm, nn, sw)
+            rows.add(mb)
+            cols.add(nb)
+        most = max(most, len(rows) + len(cols))
+    return most
+
+
+def test_select_xcd_keeps_dispatch_order_only_where_it_costs_no_panels():
+    # a grid that fills the 256 CUs once: the dispatch order when it gives no
+    # XCD more operand panels than the remap
+    for nm in (1, 2, 4, 8, 16, 32, 64, 128, 256):
+        nn = 256 // nm
+        for sw in (1, 2, 4, 8):
+            want = 0 if _busiest_xcd_panels(nm, nn, sw, False) <= _busiest_xcd_panels(nm, nn, sw, True) else 1
+            assert g.select_xcd(nm, nn, sw, 256) == want, (nm, nn, sw)
+    assert g.select_xcd(16, 16, 4, 256) == 0   # 12 panels either way (4096^2 on 256x256)
+    assert g.select_xcd(8, 32, 4, 256) == 0
+    assert g.select_xcd(32, 8, 4, 256) == 1    # 18 panels without the remap, 12 with it
+    assert g.select_xcd(4, 64, 4, 256) == 1
+    # anything but exactly one full round keeps the remap
+    for nm, nn, cus in [(20, 12, 256), (12, 12, 256), (32, 32, 256), (16, 16, 304), (16, 16, 0), (2, 2, 4096)]:
+        assert g.select_xcd(nm, nn, 4, cus) == 1, (nm, nn, cus)
+    # the answer is per shape, not left over from the previous call
+    assert [g.select_xcd(*a) for a in [(16, 16, 4, 256), (32, 8, 4, 256), (16, 16, 4, 256)]] == [0, 1, 0]
+    for args in [(0, 4, 4, 256), (4, 0, 4, 256), (4, 4, 0, 256), (4, 4, 4, -1), (1 << 16, 1 << 15, 4, 256)]:
+        with pytest.raises(g.GemmError):
+            g.select_xcd(*args)
+
+
 def test_python_wrapper_refuses_cpu_tensors():
     torch = pytest.importorskip("torch")
     a = torch.zeros(4, 8, dtype=torch.float16)
