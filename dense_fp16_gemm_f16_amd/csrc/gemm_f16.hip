@@ -327,14 +327,16 @@ int gemm_f16_select_tile(int64_t m, int64_t n, int64_t k) {
 }
 
 int gemm_f16_select_xcd(int64_t num_m, int64_t num_n, int32_t swizzle, int32_t cus) {
-    if (num_m < 1 || num_n < 1 || swizzle < 1 || cus < 0 || num_m * num_n >= (int64_t(1) << 31))
+    if (num_m < 1 || num_n < 1 || num_m > INT64_MAX / num_n || num_m * num_n >= (int64_t(1) << 31) ||
+        swizzle < 1 || cus < 0)
         return GEMM_F16_EINVAL;
     return default_xcd(num_m, num_n, swizzle, cus);
 }
 
 int gemm_f16_tile_coord(int64_t pid, int64_t num_m, int64_t num_n, int32_t swizzle, int32_t xcd,
                         int64_t *m_block, int64_t *n_block) {
-    if (num_m < 1 || num_n < 1 || swizzle < 1 || pid < 0 || pid >= num_m * num_n)
+    // the grid's size first, so that num_m * num_n cannot overflow
+    if (num_m < 1 || num_n < 1 || num_m > INT64_MAX / num_n || swizzle < 1 || pid < 0 || pid >= num_m * num_n)
         return GEMM_F16_EINVAL;
     if (!m_block || !n_block) return GEMM_F16_ENULL;
     // grids the kernels run (below 2^31 tiles) take their 32-bit arithmetic

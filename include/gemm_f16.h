@@ -158,7 +158,8 @@ const char *gemm_f16_status_string(int status);
  * gets a contiguous run of tiles; the tiles are then grouped `swizzle`
  * tile-columns wide and handed out row-major inside a group ("4. Pipeline
  * Abstraction and Two Consumer Warp Groups", section "Tile Rasterization").
- * Returns GEMM_F16_EINVAL for pid outside the grid or swizzle < 1.
+ * Returns GEMM_F16_EINVAL for num_m or num_n below 1, a grid of 2^63
+ * tiles or more, pid outside the grid or swizzle < 1.
  * Pure host function: no HIP call.
  */
 int gemm_f16_tile_coord(int64_t pid, int64_t num_m, int64_t num_n, int32_t swizzle,
@@ -178,8 +179,8 @@ int gemm_f16_select_tile(int64_t m, int64_t n, int64_t k);
  * compute units: 1 (remap) except on a grid of exactly `cus` tiles whose
  * dispatch order leaves no XCD more operand panels (distinct tile rows
  * plus tile columns) than the remap does; then 0.  Returns
- * GEMM_F16_EINVAL for num_m, num_n or swizzle below 1, cus below 0, or
- * 2^31 tiles or more.  Pure host function: no HIP call.
+ * GEMM_F16_EINVAL for num_m, num_n or swizzle below 1, cus below 0, or a
+ * grid of 2^31 tiles or more.  Pure host function: no HIP call.
  */
 int gemm_f16_select_xcd(int64_t num_m, int64_t num_n, int32_t swizzle, int32_t cus);
 

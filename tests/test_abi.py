@@ -105,7 +105,8 @@ def test_tile_coord_at_the_32_bit_boundary(nm, nn, xcd):
 
 
 def test_tile_coord_rejects_bad_input():
-    for args in [(-1, 4, 4, 1, 0), (16, 4, 4, 1, 0), (0, 4, 4, 0, 0), (0, 0, 4, 1, 0)]:
+    for args in [(-1, 4, 4, 1, 0), (16, 4, 4, 1, 0), (0, 4, 4, 0, 0), (0, 0, 4, 1, 0),
+                 (0, 1 << 40, 1 << 40, 1, 0), (0, 1 << 62, 4, 1, 0), (0, 3, 1 << 62, 1, 0)]:
         with pytest.raises(g.GemmError):
             g.tile_coord(*args)
 
@@ -154,7 +155,8 @@ def test_select_xcd_keeps_dispatch_order_only_where_it_costs_no_panels():
         assert g.select_xcd(nm, nn, 4, cus) == 1, (nm, nn, cus)
     # the answer is per shape, not left over from the previous call
     assert [g.select_xcd(*a) for a in [(16, 16, 4, 256), (32, 8, 4, 256), (16, 16, 4, 256)]] == [0, 1, 0]
-    for args in [(0, 4, 4, 256), (4, 0, 4, 256), (4, 4, 0, 256), (4, 4, 4, -1), (1 << 16, 1 << 15, 4, 256)]:
+    for args in [(0, 4, 4, 256), (4, 0, 4, 256), (4, 4, 0, 256), (4, 4, 4, -1), (1 << 16, 1 << 15, 4, 256),
+                 (1 << 40, 1 << 40, 4, 256)]:
         with pytest.raises(g.GemmError):
             g.select_xcd(*args)
 
