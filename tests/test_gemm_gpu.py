@@ -446,6 +446,23 @@ def test_schedule_options_do_not_change_bits():
     assert_bits_equal(run_gemm(a, b, tile=g.TILE_256x256), base, "repeat")
 
 
+def test_default_rasterization_on_a_grid_of_one_tile_per_cu():
+    """4096^2 on 256x256 tiles is a 16x16 grid: on a 256-CU device the
+    default keeps the dispatch order there (no XCD gets more operand panels).
+    Exact operands: bit-exact against the oracle, and the same bits with
+    either explicit setting."""
+    _announce("default rasterization, 16x16 grid")
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    assert g.select_xcd(16, 16, 4, cus) == (0 if cus == 256 else 1)
+    rng = np.random.default_rng(256)
+    a = (rng.integers(-8, 9, size=(4096, 256)) / 8).astype(np.float16)
+    b = (rng.integers(-8, 9, size=(4096, 256)) / 8).astype(np.float16)
+    base = run_gemm(a, b, tile=g.TILE_256x256)
+    assert_bits_equal(base, oracle.gemm_f16_nt(a, b), "default vs oracle")
+    for xcd in (0, 1):
+        assert_bits_equal(run_gemm(a, b, tile=g.TILE_256x256, xcd=xcd), base, f"xcd {xcd}")
+
+
 def test_torch_wrapper_on_a_side_stream():
     _announce("stream")
     rng = np.random.default_rng(5)
