@@ -146,8 +146,8 @@ constexpr uint32_t kOutOfRange = 0x80000000u;  // buffer offset past any num_rec
 #ifndef GEMM_UNIT_P_FAST
 #define GEMM_UNIT_P_FAST 0
 #endif
-// 1: the stream kernel's stores carry the streaming hint where C's rows are
-// whole 128-byte lines
+// 1: the stream kernel's stores carry the streaming hint where the host
+// asks for it (kStoreStream); 0: the default policy there instead
 #ifndef GEMM_STREAM_NT
 #define GEMM_STREAM_NT 1
 #endif
@@ -251,8 +251,31 @@ struct Params {
     int32_t k_tiles;       // ceil(k / BK)
     int32_t swizzle;
     int32_t xcd;
-    int32_t c_lines;       // fp16 C whose rows are whole 128-byte lines (N % 64 == 0, C 128-byte aligned)
+    int32_t c_store;       // cache policy of the 16-byte C stores (CStore)
 };
+
+// Cache policy of the 16-byte C stores, decided by the host per call:
+//   kStoreDevice  device scope (sc1): written through the XCD's L2 to the
+//                 memory side, where the 256 MiB Infinity Cache takes the
+//                 store bursts; chosen while A, B and C fit in it;
+//   kStoreStream  streaming (nt): C lines do not displace the A and B lines
+//                 that other workgroups of the XCD still read; for rows of
+//                 whole 128-byte lines (rows ending inside a line measured
+//                 slower with it);
+//   kStoreDefault otherwise.
+enum CStore : int32_t { kStoreDefault = 0, kStoreStream = 1, kStoreDevice = 2 };
+
+// The cache-policy operand of a buffer store for a CStore (nt = bit 1,
+// sc1 = bit 4).
+__host__ __device__ constexpr int store_aux(int pol) {
+    return pol == kStoreStream ? 2 : pol == kStoreDevice ? 16 : 0;
+}
+
+// A 16-byte global store at device scope (sc1).  No builtin carries the
+// scope bits on a global store, hence the asm.
+__device__ __forceinline__ void store_device_scope(void *dst, int4v v) {
+    asm volatile("global_store_dwordx4 %0, %1, off sc1" ::"v"(dst), "v"(v) : "memory");
+}
 
 // Block-tile configuration: BM x BN output tile, K walked 64 at a time in
 // four 16-wide k steps, WM x WN waves each owning a (BM/WM) x (BN/WN) piece
@@ -632,10 +655,11 @@ struct CStaging {
         if (m < p.m && n < p.n) {
             Out *crow = static_cast<Out *>(p.c) + (int64_t)m * p.n;
             if (vec16 && n + 16 / ES - 1 < p.n) {
-                // streaming (non-temporal) where C's rows are whole lines:
-                // the C lines then do not displace A and B lines in L2
-                // (rows that end inside a line measured slower with it)
-                if (!NN && p.c_lines)
+                // the host's cache policy (CStore; the second contract keeps
+                // the default)
+                if (!NN && p.c_store == kStoreDevice)
+                    store_device_scope(crow + n, v);
+                else if (!NN && p.c_store == kStoreStream)
                     __builtin_nontemporal_store(v, reinterpret_cast<int4v *>(crow + n));
                 else
                     *reinterpret_cast<int4v *>(crow + n) = v;
@@ -1600,7 +1624,6 @@ void gemm_f16_persistent_kernel(const Params p) {
 
     const int kt_count = p.k_tiles;  // even, >= 4 (the host's condition)
     const int ntiles = p.num_m * p.num_n;
-    const bool c_lines = (p.n * ES) % 128 == 0 && ((uintptr_t)p.c % 128) == 0;
     const int G = gridDim.x;
     int idx = blockIdx.x;
 
@@ -1821,12 +1844,14 @@ void gemm_f16_persistent_kernel(const Params p) {
                     const int r = wm * TM + pass * CS::SR + e / CS::CPR;  // row inside the tile
                     const int n = cur.n0 + wn * TN + (e % CS::CPR) * (16 / ES);
                     const uint32_t off = (n < p.n) ? (uint32_t)(r * p.n + n) * (uint32_t)ES : kOutOfRange;
-                    // rows of whole 128-byte lines: streaming (nt) stores, which keep the
-                    // C lines from displacing the A and B lines that other workgroups of
-                    // the XCD still read from L2; on rows that end inside a line they were
-                    // measured slower, so those keep the default policy
-                    if (c_lines)
-                        __builtin_amdgcn_raw_buffer_store_b128(CS::read_chunk(stg, q, el), rc, off, 0, 2);
+                    // the host's cache policy (CStore); the branch is uniform, and the
+                    // cache-policy operand must be a constant
+                    if (p.c_store == kStoreDevice)
+                        __builtin_amdgcn_raw_buffer_store_b128(CS::read_chunk(stg, q, el), rc, off, 0,
+                                                               store_aux(kStoreDevice));
+                    else if (p.c_store == kStoreStream)
+                        __builtin_amdgcn_raw_buffer_store_b128(CS::read_chunk(stg, q, el), rc, off, 0,
+                                                               store_aux(kStoreStream));
                     else
                         __builtin_amdgcn_raw_buffer_store_b128(CS::read_chunk(stg, q, el), rc, off, 0, 0);
                     __builtin_amdgcn_sched_barrier(0);  // one chunk at a time: few live registers
@@ -1879,12 +1904,9 @@ __device__ __forceinline__ void mfma16_first(half8 a, half8 b, floatx4 &c) {
 // unit's last MFMA (far more than the MFMA result latency).  Stores and
 // loads share the in-order vmcnt counter, so the step-1 acquire barrier of
 // that K-tile leaves the U stores in flight and the next K-tile's waits for
-// them.  The last tile stores its units after the loop.  NT: the stores carry the
-// streaming (non-temporal) hint, for C whose rows are whole 128-byte lines:
-// the C lines then do not displace the A and B lines that other workgroups
-// of the XCD still read from L2 (rows that end inside a line were measured
-// slower with the hint).  The host decides, so no store is behind a branch.
-template <class C, bool NT>
+// them.  The last tile stores its units after the loop.  POL: the stores'
+// cache policy (CStore), chosen by the host, so no store is behind a branch.
+template <class C, int POL>
 __global__ __launch_bounds__(C::kThreads)
 __attribute__((amdgpu_waves_per_eu(C::kMinWavesPerEU, C::kMinWavesPerEU)))
 void gemm_f16_stream_kernel(const Params p) {
@@ -2036,7 +2058,7 @@ void gemm_f16_stream_kernel(const Params p) {
         asm volatile("" : "+v"(lo), "+v"(cl));
         const uint32_t off = (lo + (uint32_t)(16 * ii * p.n + t.n0 + 32 * pp) * 2u) |
                              (t.n0 + cl + 32 * pp < p.n ? 0u : kOutOfRange);
-        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(int4v, v), rc, off, 0, NT ? 2 : 0);
+        __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(int4v, v), rc, off, 0, store_aux(POL));
     };
 
     using S0 = std::integral_constant<int, 0>;
@@ -2499,12 +2521,14 @@ hipError_t launch(const Params &p, int g, int cus, hipStream_t stream) {
                 if (GEMM_PERSIST && full && p.k_tiles % 2 == 0 && p.k_tiles >= 4 && cus > 0 && tiles > cus &&
                     p.n % 8 == 0 && ((uintptr_t)p.c % 16) == 0 && (int64_t)CD::BM * p.n * 2 < (int64_t(1) << 31)) {
                     if constexpr (GEMM_STREAM && CD::FM * CD::FN >= 16) {
-                        // rows of C that are whole 128-byte lines: streaming stores
-                        const bool lines = GEMM_STREAM_NT && p.c_lines;
-                        return lines ? launch_kernel(gemm_f16_stream_kernel<CD, true>, dim3((unsigned)cus), block,
-                                                     stream, p)
-                                     : launch_kernel(gemm_f16_stream_kernel<CD, false>, dim3((unsigned)cus), block,
-                                                     stream, p);
+                        // the C store policy is a template argument: no store
+                        // sits behind a branch
+                        const dim3 g1((unsigned)cus);
+                        if (p.c_store == kStoreDevice)
+                            return launch_kernel(gemm_f16_stream_kernel<CD, kStoreDevice>, g1, block, stream, p);
+                        if (p.c_store == kStoreStream && GEMM_STREAM_NT)
+                            return launch_kernel(gemm_f16_stream_kernel<CD, kStoreStream>, g1, block, stream, p);
+                        return launch_kernel(gemm_f16_stream_kernel<CD, kStoreDefault>, g1, block, stream, p);
                     }
                     else
                         return launch_kernel(gemm_f16_persistent_kernel<CD, false>, dim3((unsigned)cus), block, stream,
