@@ -208,8 +208,9 @@ def test_direct_to_lds_path_bit_exact(m, n, k, tile):
 # workgroup per CU walks several tiles and the K-tile stream runs across the
 # tile changes; on every block tile but 64x64 each tile's C leaves under the
 # next tile's first MFMAs, in 16-byte stores straight from the accumulators.  Ragged last tiles in M and
-# N; 1 to 5 tiles per workgroup; 4 to 10 K-tiles.  N % 64 == 0 (rows of whole
-# 128-byte lines) takes the non-temporal stores.
+# N; 1 to 5 tiles per workgroup; 4 to 10 K-tiles.  These problems fit in the
+# Infinity Cache, so C's stores are device-scope; the store policies of larger
+# problems are covered by test_store_policies_past_the_infinity_cache.
 PERSISTENT = [(g.TILE_64x64, 1100, 1064, 256), (g.TILE_64x64, 2100, 2104, 256),
               (g.TILE_128x128, 2100, 2088, 384), (g.TILE_256x256, 4200, 4152, 512),
               (g.TILE_256x128, 4200, 2088, 256), (g.TILE_128x256, 2100, 4152, 256),
@@ -225,6 +226,36 @@ def test_persistent_path_bit_exact(tile, m, n, k):
     a = (rng.integers(-8, 9, size=(m, k)) / 8).astype(np.float16)
     b = (rng.integers(-8, 9, size=(n, k)) / 8).astype(np.float16)
     assert_bits_equal(run_gemm(a, b, tile=tile), oracle.gemm_f16_nt(a, b), f"{m}x{n}x{k}")
+
+
+# The C store policies that apply only past the 256 MiB Infinity Cache (A,
+# B and C together larger): non-temporal stores on rows of whole 128-byte
+# lines, the default policy on rows that end inside a line, on the one-tile,
+# stream and one-workgroup-per-CU (64x64) kernels.  One-hot rows of A
+# (A[m, p(m)] = 1) make C[m, n] = B[n, p(m)] exactly (+0 where that is -0),
+# so the check is a gather at any size.
+PAST_THE_CACHE = [
+    (4096, 4096, 16384, g.TILE_AUTO, "one tile per workgroup, whole-line rows"),
+    (4096, 4088, 16384, g.TILE_AUTO, "one tile per workgroup, rows ending inside a line"),
+    (16384, 8200, 2048, g.TILE_AUTO, "stream kernel, rows ending inside a line"),
+    (16384, 8192, 2048, g.TILE_64x64, "one workgroup per CU on 64x64, whole-line rows"),
+    (16384, 8200, 2048, g.TILE_64x64, "one workgroup per CU on 64x64, rows ending inside a line"),
+]
+
+
+@pytest.mark.parametrize("m,n,k,tile,what", PAST_THE_CACHE)
+def test_store_policies_past_the_infinity_cache(m, n, k, tile, what):
+    _announce("store policy", what, m, n, k, tile)
+    assert (m * k + n * k) * 2 + m * n * 2 > 256 << 20
+    rng = np.random.default_rng(m + n + k)
+    p = (np.arange(m, dtype=np.int64) * 7 + 3) % k
+    a = np.zeros((m, k), np.float16)
+    a[np.arange(m), p] = 1
+    b = rng.standard_normal((n, k)).astype(np.float16)
+    got = run_gemm(a, b, tile=tile)
+    # C is a sum that starts at +0: where B holds -0, +0 + (-0) = +0
+    ref = (b[:, p].T.astype(np.float32) + np.float32(0)).astype(np.float16)
+    assert_bits_equal(got, np.ascontiguousarray(ref), what)
 
 
 # The largest K the library takes (K < 2^22): a 64x64 output, so the oracle
