@@ -49,12 +49,20 @@ static int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // ceil(K / 64): a fixed cost per launch (c), the K loop of each round (a per
 // K-tile) and a cost per tile that the one-workgroup-per-CU kernels spread
 // over the CUs (b: prologue, epilogue and C stores).  The coefficients (us)
-// are a least-squares fit, in relative error, to a sweep of every block tile
-// over 42 shapes (M, N from 512 to 16384, K 256 / 1024 / 4096) on MI355X;
-// the model picks a tile within 5% of the fastest on all of them.  Only the
-// ranking matters.  cus: compute units of the device (256 if unknown).  With
-// K % 8 != 0 the 256x256 tile would run as 128x256 (see gemm_impl), so it
-// is not a candidate.
+// are a least-squares fit, in relative error, to two sweeps of every block
+// tile over 42 shapes (M, N from 512 to 16384, K 256 / 1024 / 4096) on
+// MI355X, taking the geometric mean of the two (python -m
+// dense_fp16_gemm_f16_amd.tune --fit).  Only the ranking matters.  cus:
+// compute units of the device (256 if unknown).  With K % 8 != 0 the 256x256
+// tile would run as 128x256 (see gemm_impl), so it is not a candidate.
+//
+// The model cannot tell 256x128 from 128x256 by the matrix's orientation;
+// measured, the long side of the tile along the shorter matrix dimension
+// was the faster (8192x1024x1024: 128x256 19.8 us, 256x128 21.7;
+// 1024x8192x1024: 256x128 19.9, 128x256 21.5), so that one is taken unless
+// it needs more rounds of tiles.  With
+// it the model's tile was within 3% of the fastest on 38 of the 42 shapes
+// and within 8.2% on all of them.
 static int auto_tile(int64_t m, int64_t n, int64_t k, int cus) {
     if (cus <= 0) cus = 256;
     struct Cand {
@@ -62,13 +70,13 @@ static int auto_tile(int64_t m, int64_t n, int64_t k, int cus) {
         double c, a, b;
     };
     static const Cand cands[] = {
-        {GEMM_F16_TILE_256x256, 256, 256, 7.58, 1.075, 8.35},
-        {GEMM_F16_TILE_256x128, 256, 128, 5.78, 0.644, 3.73},
-        {GEMM_F16_TILE_128x256, 128, 256, 5.70, 0.645, 3.95},
-        {GEMM_F16_TILE_128x128, 128, 128, 4.53, 0.431, 1.69},
-        {GEMM_F16_TILE_128x64, 128, 64, 3.49, 0.385, 1.02},
-        {GEMM_F16_TILE_64x128, 64, 128, 3.70, 0.387, 0.934},
-        {GEMM_F16_TILE_64x64, 64, 64, 3.35, 0.308, 0.465},
+        {GEMM_F16_TILE_256x256, 256, 256, 8.280, 1.115, 6.212},
+        {GEMM_F16_TILE_256x128, 256, 128, 5.825, 0.663, 3.036},
+        {GEMM_F16_TILE_128x256, 128, 256, 5.856, 0.661, 2.886},
+        {GEMM_F16_TILE_128x128, 128, 128, 4.492, 0.436, 1.517},
+        {GEMM_F16_TILE_128x64, 128, 64, 3.479, 0.385, 0.845},
+        {GEMM_F16_TILE_64x128, 64, 128, 3.545, 0.391, 0.780},
+        {GEMM_F16_TILE_64x64, 64, 64, 3.254, 0.308, 0.315},
     };
     const int64_t k_tiles = cdiv(k, 64);
     int best = GEMM_F16_TILE_64x64;
@@ -82,6 +90,13 @@ static int auto_tile(int64_t m, int64_t n, int64_t k, int cus) {
             best_t = t;
             best = c.id;
         }
+    }
+    if ((best == GEMM_F16_TILE_256x128 || best == GEMM_F16_TILE_128x256) && m != n) {
+        // rounds of tiles on 128 x 256 (wide) or 256 x 128
+        auto rounds = [&](bool wide) { return cdiv(cdiv(m, wide ? 128 : 256) * cdiv(n, wide ? 256 : 128), cus); };
+        const bool wide = m > n;
+        if (rounds(wide) <= rounds(best == GEMM_F16_TILE_128x256))
+            best = wide ? GEMM_F16_TILE_128x256 : GEMM_F16_TILE_256x128;
     }
     return best;
 }

@@ -4,6 +4,7 @@
     python -m dense_fp16_gemm_f16_amd.tune --data      # operand values vs time
     python -m dense_fp16_gemm_f16_amd.tune --ceiling   # MFMA rate, no HBM traffic
     python -m dense_fp16_gemm_f16_amd.tune --graph 100 # eager launches vs one HIP graph
+    python -m dense_fp16_gemm_f16_amd.tune --fit SWEEP.jsonl [...]  # refit the tile model
 
 For every shape (default: the five benchmark workloads) it times each block
 tile (and, for the default tile, a few swizzle widths) with HIP events,
@@ -16,6 +17,7 @@ from __future__ import annotations
 
 import argparse
 import json
+import math
 import statistics
 import sys
 
@@ -42,10 +44,16 @@ def main(argv=None) -> int:
                     help="with --data or --ceiling: run each operand set (or probe variant) back to back "
                          "for this long and print its wall-clock start and end (to line up with power and "
                          "clock samples)")
+    ap.add_argument("--fit", nargs="+", default=None, metavar="SWEEP",
+                    help="instead (no GPU): fit the automatic tile choice's model to sweep files of this "
+                         "tool (the geometric mean over the files), print its coefficients and its choice "
+                         "against the fastest tile on every shape")
     ap.add_argument("--graph", type=int, default=0, metavar="N",
                     help="instead: time N GEMMs of each shape (default 256^3, 1024^3, 2048^3) launched "
                          "eagerly and replayed from one captured HIP graph")
     a = ap.parse_args(argv)
+    if a.fit:
+        return fit_model(a.fit)
     import torch
 
     if a.graph:
@@ -294,6 +302,85 @@ def ceiling(a, torch) -> int:
             print(json.dumps({"probe": probes[variant] + ", 128x128 wave tile", "variant": names[variant],
                               "operands": operands, "workgroups": wgs, "ms": round(med, 2),
                               "tflops": round(tf, 1)}), flush=True)
+    return 0
+
+
+
+# The automatic tile choice's candidates (tile id: block tile), the same list
+# and order as auto_tile in csrc/gemm_f16.hip.
+MODEL_TILES = {g.TILE_256x256: (256, 256), g.TILE_256x128: (256, 128), g.TILE_128x256: (128, 256),
+               g.TILE_128x128: (128, 128), g.TILE_128x64: (128, 64), g.TILE_64x128: (64, 128),
+               g.TILE_64x64: (64, 64)}
+
+
+def _cdiv(a: int, b: int) -> int:
+    return -(-a // b)
+
+
+def model_terms(tile: int, m: int, n: int, k: int, cus: int = 256) -> tuple[float, float, float]:
+    """The model's three terms for one block tile: 1, rounds * k_tiles, tiles / cus."""
+    bm, bn = MODEL_TILES[tile]
+    tiles = _cdiv(m, bm) * _cdiv(n, bn)
+    return 1.0, float(_cdiv(tiles, cus) * _cdiv(k, 64)), tiles / cus
+
+
+def model_choice(coef: dict, m: int, n: int, k: int, cus: int = 256) -> int:
+    """The tile auto_tile picks with coefficients coef {tile: (c, a, b)}: the
+    smallest modelled time, then a rectangular tile turned with its long side
+    along the shorter dimension unless that costs a round of tiles."""
+    best, best_t = g.TILE_64x64, 1e300
+    for tile in MODEL_TILES:
+        if tile == g.TILE_256x256 and k % 8 != 0:
+            continue
+        t = sum(x * y for x, y in zip(coef[tile], model_terms(tile, m, n, k, cus)))
+        if t < best_t * 0.999:
+            best, best_t = tile, t
+    if best in (g.TILE_256x128, g.TILE_128x256) and m != n:
+        def rounds(wide):
+            return _cdiv(_cdiv(m, 128 if wide else 256) * _cdiv(n, 256 if wide else 128), cus)
+        wide = m > n
+        if rounds(wide) <= rounds(best == g.TILE_128x256):
+            best = g.TILE_128x256 if wide else g.TILE_256x128
+    return best
+
+
+def fit_model(paths: list[str]) -> int:
+    """Least squares in relative error, per candidate tile, of the time model
+    to the default-rasterization times of sweep files (geometric mean over
+    the files where a shape and tile appear in all of them)."""
+    import numpy as np
+
+    runs = []
+    for path in paths:
+        times = {}
+        with open(path) as f:
+            for line in f:
+                r = json.loads(line)
+                if "best" in r or r.get("swizzle") != 0 or r.get("variant", 0) != 0:
+                    continue
+                times[(tuple(r["shape"]), r["tile"])] = r["us"]
+        runs.append(times)
+    keys = set(runs[0]).intersection(*runs[1:])
+    mean = {key: math.exp(statistics.fmean(math.log(t[key]) for t in runs)) for key in keys}
+    shapes = sorted({s for s, _ in mean})
+    coef = {}
+    for tile in MODEL_TILES:
+        rows = [[x / mean[(s, tile)] for x in model_terms(tile, *s)] for s in shapes if (s, tile) in mean]
+        coef[tile] = tuple(float(v) for v in np.linalg.lstsq(np.array(rows), np.ones(len(rows)), rcond=None)[0])
+    names = {t: f"{bm}x{bn}" if t in MODEL_TILES else f"{bm}x{bn} (tile {t})" for t, (bm, bn) in g.TILES.items()}
+    for tile, (c, a_, b) in coef.items():
+        print(json.dumps({"tile": tile, "block": names[tile], "c": round(c, 3), "a": round(a_, 3), "b": round(b, 3)}))
+    ratios = []
+    for s in shapes:
+        have = {t: mean[(s, t)] for t in g.TILES if (s, t) in mean}  # every tile swept, candidates or not
+        fastest = min(have, key=have.get)
+        pick = model_choice(coef, *s)
+        ratios.append(have[pick] / have[fastest])
+        print(json.dumps({"shape": list(s), "fastest": names[fastest], "fastest_us": round(have[fastest], 2),
+                          "model": names[pick], "model_us": round(have[pick], 2),
+                          "ratio": round(ratios[-1], 3)}))
+    print(json.dumps({"shapes": len(ratios), "within_3pct": sum(r <= 1.03 for r in ratios),
+                      "within_5pct": sum(r <= 1.05 for r in ratios), "worst": round(max(ratios), 3)}))
     return 0
 
 
