@@ -655,9 +655,9 @@ struct CStaging {
         if (m < p.m && n < p.n) {
             Out *crow = static_cast<Out *>(p.c) + (int64_t)m * p.n;
             if (vec16 && n + 16 / ES - 1 < p.n) {
-                // the host's cache policy (CStore; the second contract keeps
-                // the default)
-                if (!NN && p.c_store == kStoreDevice)
+                // the host's cache policy (CStore; past the cache the second
+                // contract keeps the default)
+                if (p.c_store == kStoreDevice)
                     store_device_scope(crow + n, v);
                 else if (!NN && p.c_store == kStoreStream)
                     __builtin_nontemporal_store(v, reinterpret_cast<int4v *>(crow + n));
