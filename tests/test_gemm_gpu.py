@@ -465,6 +465,21 @@ def test_k_zero_writes_zeros_and_empty_is_a_no_op():
     assert run_gemm(np.ones((9, 16), np.float16), np.zeros((0, 16), np.float16)).shape == (9, 0)
 
 
+@pytest.mark.parametrize("tile", TILES)
+def test_a_sum_of_zeros_is_positive_zero(tile):
+    """Every product -0 (one-hot A against -0, and zeros against negative
+    numbers): C is +0, since the fp32 sum starts at +0 and +0 + (-0) = +0."""
+    _announce("signed zero", tile)
+    m, n, k = 70, 40, 128
+    a = np.zeros((m, k), np.float16)
+    a[:, 0] = 1
+    b = -np.abs(np.random.default_rng(7).standard_normal((n, k))).astype(np.float16)
+    b[:, 0] = -0.0
+    got = run_gemm(a, b, tile=tile)
+    assert np.all(got.view(np.uint16) == 0), "C must be +0"
+    assert_bits_equal(got, oracle.gemm_f16_nt(a, b), "signed zero")
+
+
 def test_schedule_options_do_not_change_bits():
     """Rasterization only reorders tiles; each output's sum order is fixed."""
     _announce("determinism")

@@ -98,6 +98,16 @@ def test_one_hot_rows_select_columns_of_b():
     assert np.array_equal(c.view(np.uint16), b[:, p].T.copy().view(np.uint16))
 
 
+def test_a_sum_of_zeros_is_positive_zero():
+    # C is a sum that starts at +0: with every product -0 (1 * -0 and
+    # 0 * negative numbers) it stays +0, since +0 + (-0) = +0 under
+    # round-to-nearest; a sum started at -0 would give -0
+    a = np.array([[1.0, 0.0, 0.0], [0.0, 0.0, 0.0]], dtype=np.float16)
+    b = np.array([[-0.0, -1.0, -2.0], [0.0, 1.0, 2.0]], dtype=np.float16)
+    c = oracle.gemm_f16_nt(a, b).view(np.uint16)
+    assert c.tolist() == [[0x0000, 0x0000], [0x0000, 0x0000]]
+
+
 def test_row_sums_and_rank_one():
     rng = np.random.default_rng(6)
     k = 64

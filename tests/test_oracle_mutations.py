@@ -31,6 +31,7 @@ MUTANTS = {
     "subnormal_threshold": ("if (e < -14)", "if (e < -15)"),
     "nn_b_read_as_n_by_k": ("j->table[j->b[ki * j->n + ni]]", "j->table[j->b[(ni * j->k + ki) % (j->n * j->k)]]"),
     "nn_abs_dropped": ("sabs += fabs(prod);", "sabs += prod;"),
+    "sum_starts_at_negative_zero": ("double sum = 0.0;", "double sum = -0.0;"),
     "nn_sum_skips_first": ("for (int64_t ki = 0; ki < j->k; ++ki) {\n                const double prod",
                            "for (int64_t ki = 1; ki < j->k; ++ki) {\n                const double prod"),
 }
@@ -67,6 +68,10 @@ def _pin_failures(orc):
     b = np.array([[32.0, 16.0]], dtype=np.float16)  # 65504 + 16 = 65520: the overflow tie
     if orc.gemm_f16_nt(a, b).view(np.uint16)[0, 0] != 0x7C00:
         fails.append("overflow_tie")
+    a = np.array([[1.0, 0.0, 0.0]], dtype=np.float16)
+    b = np.array([[-0.0, -1.0, -2.0]], dtype=np.float16)  # every product -0
+    if orc.gemm_f16_nt(a, b).view(np.uint16)[0, 0] != 0x0000:
+        fails.append("signed_zero")
     for k in (1000, 4096):
         if not np.all(orc.gemm_f16_nt(np.ones((2, k), np.float16), np.ones((3, k), np.float16))
                       == np.float16(k)):
