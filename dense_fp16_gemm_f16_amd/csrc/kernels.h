@@ -2070,13 +2070,15 @@ void gemm_f16_stream_kernel(const Params p) {
     constexpr int L0 = L * GEMM_AHEAD_STEP0_LOADS / 16;  // loads of K-tile t+2 in step 0
     static_assert(U + L0 < 64, "vmcnt range");
 
-    // Prologue: K-tiles 0 and 1 into stages 0 and 1, both in LDS before the
-    // first K-tile; both steps' fragments of K-tile 0 into buffers 0 and 1.
+    // Prologue: K-tiles 0 and 1 into stages 0 and 1; wait for K-tile 0 only
+    // (K-tile 1's loads went out first, so the first K-tile's acquire
+    // barrier, vmcnt(U + L0), covers them); both steps' fragments of K-tile
+    // 0 into buffers 0 and 1.
 #pragma unroll
     for (int i = 0; i < L; ++i) load(S0{}, 0, i);
 #pragma unroll
     for (int i = 0; i < L; ++i) load(S1{}, 1, i);
-    vm_barrier<0>();
+    vm_barrier<L>();
     GEMM_TRACE_DO(tr.t1 = trace_clock();)
 #pragma unroll
     for (int r = 0; r < NR; ++r) read_frag(0, 0, 0, r);
