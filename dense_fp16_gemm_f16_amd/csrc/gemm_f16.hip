@@ -60,9 +60,8 @@ static int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 // measured, the long side of the tile along the shorter matrix dimension
 // was the faster (8192x1024x1024: 128x256 19.8 us, 256x128 21.7;
 // 1024x8192x1024: 256x128 19.9, 128x256 21.5), so that one is taken unless
-// it needs more rounds of tiles.  With
-// it the model's tile was within 3% of the fastest on 38 of the 42 shapes
-// and within 8.2% on all of them.
+// it needs more rounds of tiles.  With that, the model's tile was within 3%
+// of the fastest on 38 of the 42 shapes and within 8.2% on all of them.
 static int auto_tile(int64_t m, int64_t n, int64_t k, int cus) {
     if (cus <= 0) cus = 256;
     struct Cand {
