@@ -329,6 +329,95 @@ def cpu_baseline(a, b, c_gpu, w, budget_s: float):
     return rec, parity
 
 
+def summarize(args, results: list) -> dict:
+    """The JSON record from the children's results (everything but the CPU
+    baseline and the parity checks, which need the inputs and outputs)."""
+    from dense_fp16_gemm_f16_amd import inputs
+
+    w = inputs.WORKLOADS[args.workload]
+    nn = w.b_layout == "kn"
+    flops = float(w.flops)
+    per_proc = []
+    for r in results:
+        h = r["headline"]
+        per_proc.append({"value": flops * args.steps / h["wall_s"] / 1e12,
+                         "ms_per_step": h["wall_s"] * 1e3 / args.steps,
+                         "kernel_avg_us": statistics.mean(h["kernel_us"]),
+                         "kernel_median_us": statistics.median(h["kernel_us"])})
+    mid = sorted(range(len(per_proc)), key=lambda i: per_proc[i]["value"])[len(per_proc) // 2]
+    med = per_proc[mid]
+    avg_us = statistics.median(p["kernel_avg_us"] for p in per_proc)
+    achieved = flops / (avg_us * 1e-6) / 1e12
+    log(f"headline per process: " + ", ".join(f"{p['value']:.1f}" for p in per_proc) + " TFLOP/s")
+
+    rec = {
+        "metric": METRIC,
+        "value": round(med["value"], 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(med["ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",  # fp16 operands; the accumulation (fp32) is named in the metric
+        "data": "synthetic",
+        "config": {"workload": w.name, "m": w.m, "n": w.n, "k": w.k, "values": w.dist,
+                   "tile": results[mid]["headline"]["tile"]},
+        "timing": {"processes": len(per_proc),
+                   "value_per_process": [round(p["value"], 2) for p in per_proc],
+                   "statistic": "median over fresh processes of the K-step wall-clock rate"},
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(achieved, 2),
+            "peak": PEAK_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_TFLOPS, 4),
+            "traffic": measured_traffic(w.name),
+            "kernel_avg_us": round(avg_us, 2),
+            "kernel_median_us": round(statistics.median(p["kernel_median_us"] for p in per_proc), 2),
+        },
+        "cpu_baseline": None,
+    }
+    if all("sustained" in r for r in results):
+        rates = [flops * r["sustained"]["launches"] / r["sustained"]["seconds"] / 1e12 for r in results]
+        rec["sustained"] = {"tflops": round(statistics.median(rates), 2),
+                            "tflops_per_process": [round(x, 2) for x in rates],
+                            "seconds": round(statistics.median(r["sustained"]["seconds"] for r in results), 3),
+                            "launches": results[0]["sustained"]["launches"]}
+    cs = results[0].get("cold_start")
+    if cs:
+        rec["cold_start"] = {"tflops": round(flops * args.steps / cs["wall_s"] / 1e12, 2),
+                             "kernel_avg_us": round(statistics.mean(cs["kernel_us"]), 2),
+                             "what": f"the first process's first {args.warmup} + {args.steps} steps, "
+                                     "on a device that was idle"}
+    cold = statistics.median(statistics.median(r["cold_kernel_us"]) for r in results)
+    rec["cold_cache"] = {"kernel_median_us": round(cold, 2), "tflops": round(flops / (cold * 1e-6) / 1e12, 2),
+                         "flush": "512 MiB written before each launch"}
+    cfgs = []
+    for name in CONFIGS:
+        cw = inputs.WORKLOADS[name]
+        per = [statistics.median(r["configs"][name]["kernel_us"]) for r in results]
+        us = statistics.median(per)
+        tf = cw.flops / (us * 1e-6) / 1e12
+        cfg = {"workload": name, "m": cw.m, "n": cw.n, "k": cw.k, "values": cw.dist,
+               "tile": results[0]["configs"][name]["tile"], "kernel_median_us": round(us, 2),
+               "tflops": round(tf, 1), "frac": round(tf / PEAK_TFLOPS, 4),
+               "traffic": measured_traffic(name)}
+        if name == w.name and "sustained" in rec:
+            cfg["sustained_tflops"] = rec["sustained"]["tflops"]
+        elif all("sustained" in r["configs"][name] for r in results):
+            cfg["sustained_tflops"] = round(statistics.median(
+                cw.flops * r["configs"][name]["sustained"]["launches"]
+                / r["configs"][name]["sustained"]["seconds"] / 1e12 for r in results), 1)
+        cfgs.append(cfg)
+    rec["configs"] = cfgs
+    if nn:
+        rec["metric"] = "fp16 GEMM D = A*B (B [K,N], fp32 out) TFLOP/s; % of MI355X dense fp16 MFMA peak"
+    return rec
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -403,87 +492,10 @@ def main() -> int:
             with open(os.path.join(tmp, f"result_{i}.json")) as f:
                 results.append(json.load(f))
 
+        rec = summarize(args, results)
         w = inputs.WORKLOADS[args.workload]
         nn = w.b_layout == "kn"
-        flops = float(w.flops)
-        per_proc = []
-        for r in results:
-            h = r["headline"]
-            per_proc.append({"value": flops * args.steps / h["wall_s"] / 1e12,
-                             "ms_per_step": h["wall_s"] * 1e3 / args.steps,
-                             "kernel_avg_us": statistics.mean(h["kernel_us"]),
-                             "kernel_median_us": statistics.median(h["kernel_us"])})
-        mid = sorted(range(len(per_proc)), key=lambda i: per_proc[i]["value"])[len(per_proc) // 2]
-        med = per_proc[mid]
-        avg_us = statistics.median(p["kernel_avg_us"] for p in per_proc)
-        achieved = flops / (avg_us * 1e-6) / 1e12
-        log(f"headline per process: " + ", ".join(f"{p['value']:.1f}" for p in per_proc) + " TFLOP/s")
-
-        rec = {
-            "metric": METRIC,
-            "value": round(med["value"], 2),
-            "unit": "TFLOP/s",
-            "n_gpus": 1,
-            "steps": args.steps,
-            "warmup": args.warmup,
-            "ms_per_step": round(med["ms_per_step"], 5),
-            "higher_is_better": True,
-            "scaling": "weak",
-            "vs_baseline": None,
-            "dtype": "f16",  # fp16 operands; the accumulation (fp32) is named in the metric
-            "data": "synthetic",
-            "config": {"workload": w.name, "m": w.m, "n": w.n, "k": w.k, "values": w.dist,
-                       "tile": results[mid]["headline"]["tile"]},
-            "timing": {"processes": len(per_proc),
-                       "value_per_process": [round(p["value"], 2) for p in per_proc],
-                       "statistic": "median over fresh processes of the K-step wall-clock rate"},
-            "roofline": {
-                "bound": "mfma",
-                "achieved": round(achieved, 2),
-                "peak": PEAK_TFLOPS,
-                "unit": "TFLOP/s",
-                "frac": round(achieved / PEAK_TFLOPS, 4),
-                "traffic": measured_traffic(w.name),
-                "kernel_avg_us": round(avg_us, 2),
-                "kernel_median_us": round(statistics.median(p["kernel_median_us"] for p in per_proc), 2),
-            },
-            "cpu_baseline": None,
-        }
-        if all("sustained" in r for r in results):
-            rates = [flops * r["sustained"]["launches"] / r["sustained"]["seconds"] / 1e12 for r in results]
-            rec["sustained"] = {"tflops": round(statistics.median(rates), 2),
-                                "tflops_per_process": [round(x, 2) for x in rates],
-                                "seconds": round(statistics.median(r["sustained"]["seconds"] for r in results), 3),
-                                "launches": results[0]["sustained"]["launches"]}
-        cs = results[0].get("cold_start")
-        if cs:
-            rec["cold_start"] = {"tflops": round(flops * args.steps / cs["wall_s"] / 1e12, 2),
-                                 "kernel_avg_us": round(statistics.mean(cs["kernel_us"]), 2),
-                                 "what": f"the first process's first {args.warmup} + {args.steps} steps, "
-                                         "on a device that was idle"}
-        cold = statistics.median(statistics.median(r["cold_kernel_us"]) for r in results)
-        rec["cold_cache"] = {"kernel_median_us": round(cold, 2), "tflops": round(flops / (cold * 1e-6) / 1e12, 2),
-                             "flush": "512 MiB written before each launch"}
-        cfgs = []
-        for name in CONFIGS:
-            cw = inputs.WORKLOADS[name]
-            per = [statistics.median(r["configs"][name]["kernel_us"]) for r in results]
-            us = statistics.median(per)
-            tf = cw.flops / (us * 1e-6) / 1e12
-            cfg = {"workload": name, "m": cw.m, "n": cw.n, "k": cw.k, "values": cw.dist,
-                   "tile": results[0]["configs"][name]["tile"], "kernel_median_us": round(us, 2),
-                   "tflops": round(tf, 1), "frac": round(tf / PEAK_TFLOPS, 4),
-                   "traffic": measured_traffic(name)}
-            if name == w.name and "sustained" in rec:
-                cfg["sustained_tflops"] = rec["sustained"]["tflops"]
-            elif all("sustained" in r["configs"][name] for r in results):
-                cfg["sustained_tflops"] = round(statistics.median(
-                    cw.flops * r["configs"][name]["sustained"]["launches"]
-                    / r["configs"][name]["sustained"]["seconds"] / 1e12 for r in results), 1)
-            cfgs.append(cfg)
-        rec["configs"] = cfgs
-        if nn:
-            rec["metric"] = "fp16 GEMM D = A*B (B [K,N], fp32 out) TFLOP/s; % of MI355X dense fp16 MFMA peak"
+        cfgs = rec["configs"]
 
         if args.cpu_budget > 0 and not nn:
             import oracle
