@@ -74,3 +74,14 @@ def test_sustained_cold_and_configs(record):
         assert c["tflops"] == pytest.approx(1000, rel=2e-3)
         assert c["frac"] == pytest.approx(0.4, rel=2e-3)
         assert c["sustained_tflops"] == pytest.approx(800, rel=2e-3)
+
+
+def test_more_than_one_gpu_is_refused_with_a_message():
+    import os
+    import subprocess
+    import sys
+
+    r = subprocess.run([sys.executable, os.path.abspath(bench.__file__), "--gpus", "2"],
+                       capture_output=True, text=True, timeout=120)
+    assert r.returncode == 2 and r.stdout == ""
+    assert "one GPU" in r.stderr
