@@ -85,3 +85,34 @@ def test_more_than_one_gpu_is_refused_with_a_message():
                        capture_output=True, text=True, timeout=120)
     assert r.returncode == 2 and r.stdout == ""
     assert "one GPU" in r.stderr
+
+
+def test_parity_helpers_match_the_tests_bar():
+    import numpy as np
+
+    from tests import pins
+
+    rng = np.random.default_rng(3)
+    ref = np.concatenate([rng.standard_normal(2000) * 10.0 ** rng.integers(-6, 4, 2000), [0.0, 6e-8, 65504.0]])
+    for k in (256, 1000, 8192):
+        assert np.array_equal(bench.ulp_tolerance(ref, k), pins.ulp_tolerance(ref, k))
+
+    w_exact = inputs.WORKLOADS["gemm_256_eighths"]
+    ref16 = (rng.integers(-64, 65, 500) / 8).astype(np.float16)
+    got16 = ref16.copy()
+    assert bench.compare(got16, ref16, w_exact)["ok"]
+    got16.view(np.uint16)[7] ^= 1
+    r = bench.compare(got16, ref16, w_exact)
+    assert not r["ok"] and r["mismatches"] == 1
+
+    w_ulp = inputs.WORKLOADS["gemm_4096_normal"]
+    ref16 = rng.standard_normal(500).astype(np.float16)
+    tol = bench.ulp_tolerance(ref16.astype(np.float64), w_ulp.k)
+    assert bench.compare(ref16.copy(), ref16, w_ulp)["worst_err_over_tol"] == 0.0
+    near = (ref16.astype(np.float64) + 0.9 * tol).astype(np.float32)
+    assert bench.compare(near, ref16, w_ulp)["ok"]
+    far = (ref16.astype(np.float64) + 1.1 * tol).astype(np.float32)
+    assert not bench.compare(far, ref16, w_ulp)["ok"]
+    bad = ref16.astype(np.float32)
+    bad[3] = np.nan
+    assert not bench.compare(bad, ref16, w_ulp)["ok"]
