@@ -58,6 +58,11 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
+def _csv_rows(path: str) -> list:
+    with open(path, newline="") as f:
+        return list(csv.DictReader(f))
+
+
 def _one(pattern: str) -> str:
     """The one file matching `pattern`; a folder that holds several runs is
     ambiguous and raises rather than reading whichever sorts first."""
@@ -71,7 +76,7 @@ def _one(pattern: str) -> str:
 
 def kernel_stats(d: str, kernel: str) -> dict:
     path = _one(os.path.join(d, "**", "*kernel_stats.csv"))
-    for r in csv.DictReader(open(path)):
+    for r in _csv_rows(path):
         if kernel in r["Name"]:
             return {"name": r["Name"], "calls": int(r["Calls"]), "avg_us": float(r["AverageNs"]) / 1e3,
                     "min_us": float(r["MinNs"]) / 1e3, "max_us": float(r["MaxNs"]) / 1e3}
@@ -82,7 +87,7 @@ def kernel_window(d: str, kernel: str, min_us: float, skip: int, count: int) -> 
     """Durations of the launches of `kernel` lasting at least min_us, in dispatch
     order, after the first `skip` of them: `count` launches."""
     path = _one(os.path.join(d, "**", "*kernel_trace.csv"))
-    rows = [r for r in csv.DictReader(open(path)) if kernel in r["Kernel_Name"]]
+    rows = [r for r in _csv_rows(path) if kernel in r["Kernel_Name"]]
     rows.sort(key=lambda r: int(r["Start_Timestamp"]))
     durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3 for r in rows]
     durs = [x for x in durs if x >= min_us]
@@ -96,7 +101,7 @@ def kernel_window(d: str, kernel: str, min_us: float, skip: int, count: int) -> 
 def counter_per_dispatch(d: str, kernel: str, counter: str) -> list[float]:
     path = _one(os.path.join(d, "**", "*counter_collection.csv"))
     per = {}
-    for r in csv.DictReader(open(path)):
+    for r in _csv_rows(path):
         if kernel in r["Kernel_Name"] and r["Counter_Name"] == counter:
             per[int(r["Dispatch_Id"])] = per.get(int(r["Dispatch_Id"]), 0.0) + float(r["Counter_Value"])
     return [per[k] for k in sorted(per)]
@@ -105,7 +110,7 @@ def counter_per_dispatch(d: str, kernel: str, counter: str) -> list[float]:
 def counters(d: str, kernel: str) -> dict:
     """Every counter of a --pmc run, per dispatch of `kernel`."""
     path = _one(os.path.join(d, "**", "*counter_collection.csv"))
-    names = sorted({r["Counter_Name"] for r in csv.DictReader(open(path)) if kernel in r["Kernel_Name"]})
+    names = sorted({r["Counter_Name"] for r in _csv_rows(path) if kernel in r["Kernel_Name"]})
     out = {c: counter_per_dispatch(d, kernel, c) for c in names}
     if "SQ_VALU_MFMA_BUSY_CYCLES" in out and "GRBM_GUI_ACTIVE" in out:
         out["mfma_busy_share"] = [round(b / 1024.0 / (g / 8.0), 4) for b, g in

@@ -56,7 +56,8 @@ def _notes(elf: bytes):
 
 def kernel_records(lib_path: str, arch: str = "gfx950") -> list[dict]:
     """One metadata record per kernel of every `arch` code object in the library."""
-    blob = open(lib_path, "rb").read()
+    with open(lib_path, "rb") as f:
+        blob = f.read()
     out = []
     for triple, obj in _bundles(blob):
         if not triple.startswith("hip") or arch not in triple:

@@ -19,7 +19,8 @@ HEADER = os.path.join(ROOT, "include", "gemm_f16.h")
 
 
 def _declared_functions():
-    text = open(HEADER).read()
+    with open(HEADER) as f:
+        text = f.read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(gemm_f16_\w+)\s*\(", text)))
 

@@ -45,7 +45,8 @@ def test_lds_fits_the_cu(records):
 
 @pytest.mark.skipif(not os.path.exists(OBJDUMP), reason="llvm-objdump not installed")
 def test_no_packed_fp32_instructions():
-    blob = open(g.LIB_PATH, "rb").read()
+    with open(g.LIB_PATH, "rb") as f:
+        blob = f.read()
     found, mfma = [], 0
     with tempfile.TemporaryDirectory() as d:
         for i, (triple, obj) in enumerate(_codeobj._bundles(blob)):

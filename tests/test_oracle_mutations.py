@@ -101,7 +101,8 @@ def test_unmutated_oracle_passes_every_pin():
 @pytest.mark.parametrize("name", sorted(MUTANTS))
 def test_planted_mistake_is_caught(name, tmp_path):
     old, new = MUTANTS[name]
-    src = open(SRC).read()
+    with open(SRC) as f:
+        src = f.read()
     assert src.count(old) == 1, f"mutation site for {name} not unique"
     path = tmp_path / "gemm_ref_mutant.c"
     path.write_text(src.replace(old, new))

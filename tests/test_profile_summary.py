@@ -42,7 +42,8 @@ def test_source_hash_of_the_library_is_recorded_in_the_traffic_files():
     files = glob.glob(os.path.join(root, "profiles", "traffic_*.json"))
     assert files
     for p in files:
-        rec = json.load(open(p))
+        with open(p) as f:
+            rec = json.load(f)
         assert len(rec["kernel_source_sha256_16"]) == 16
         assert rec["hbm_bytes_per_launch"] > 0
 

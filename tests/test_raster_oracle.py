@@ -14,7 +14,8 @@ GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "raster_worked_exampl
 
 
 def test_worked_example_strip_counts():
-    g = json.load(open(GOLDEN))
+    with open(GOLDEN) as f:
+        g = json.load(f)
     nm, nn, active, sw = g["num_m_blocks"], g["num_n_blocks"], g["active_blocks"], g["swizzle_size"]
     plain = [raster.plain_2d_coord(p, nm, nn) for p in range(active)]
     swz = [raster.swizzle_tile_coord(p, nm, nn, sw) for p in range(active)]

@@ -14,7 +14,8 @@ SRC = os.path.join(os.path.dirname(g.__file__), "csrc", "gemm_f16.hip")
 
 
 def library_coefficients():
-    text = open(SRC).read()
+    with open(SRC) as f:
+        text = f.read()
     rows = re.findall(r"\{GEMM_F16_TILE_(\w+), (\d+), (\d+), ([\d.]+), ([\d.]+), ([\d.]+)\}", text)
     coef = {}
     for name, bm, bn, c, a, b in rows:
