@@ -288,15 +288,14 @@ static int gemm_impl(bool nn, int64_t m, int64_t n, int64_t k, const void *a, co
         return e == hipSuccess ? GEMM_F16_OK : GEMM_F16_EHIP;
     }
 
-    // Elements per global load: 16-byte loads need 16-byte aligned rows of
-    // A, and of B in its layout; for C = A B^T, 8- and 4-byte loads serve
-    // rows aligned to 8 or 4 bytes; otherwise one element per load.
+    // The operands' row alignment: 16-byte aligned rows of A, and of B in
+    // its layout, take the direct-to-LDS loads; for C = A B^T, rows aligned
+    // to 4 bytes take 16-byte loads at 4-byte aligned offsets; otherwise
+    // (2-byte aligned rows) 16-byte loads shifted into place.
     const uintptr_t ab = (uintptr_t)a | (uintptr_t)b;
     int g = 1;
     if ((k % 8) == 0 && (!nn || (n % 8) == 0) && (ab % 16) == 0)
         g = 8;
-    else if (!nn && (k % 4) == 0 && (ab % 8) == 0)
-        g = 4;
     else if (!nn && (k % 2) == 0 && (ab % 4) == 0)
         g = 2;
 

@@ -15,8 +15,9 @@
 //               buffer_load_dwordx4 ... lds straight into a 2-stage LDS ring
 //               (KMajorDirect: 1 KB = 8 rows of 128 bytes per wave
 //               instruction; lanes past K get an out-of-range offset and
-//               land as zeros).  Otherwise 16/8/4/2-byte loads staged in
-//               VGPRs one K-tile ahead (KMajorOperand).  Buffer descriptors
+//               land as zeros).  Otherwise 16-byte loads at 4-byte aligned
+//               offsets (shifted into place on 2-byte aligned rows) staged
+//               in VGPRs one K-tile ahead (KMajorOperand).  Buffer descriptors
 //               bound each operand tile, so rows past M / N read as zero;
 //  * LDS        direct path: 128-byte rows with the 16-byte chunks
 //               swizzled by the row index, conflict-free fragment reads;
@@ -354,14 +355,21 @@ __device__ __forceinline__ void lds_barrier() {
 // GEMM_PLANE_PAD bytes.  Each pass of the workgroup covers RPP rows of the
 // K-tile (ROWS x 64 fp16 = ROWS x 8 chunks of 16 bytes); thread t owns
 // chunk t % 8 of rows t / 8 + RPP * i, so every 8 consecutive lanes read one
-// 128-byte row segment.  G: fp16 elements per global load, the largest the
-// alignment of the rows allows: 8 (one 16-byte load per chunk), 4 (two
-// 8-byte loads), 2 (four 4-byte loads) or 1 (eight 2-byte loads).
+// 128-byte row segment.  G says how the rows are aligned:
+//   8: 16-byte aligned rows (K % 8 == 0): one 16-byte load per chunk;
+//   2: 4-byte aligned rows (K even): one 16-byte load per chunk at a 4-byte
+//      aligned offset;
+//   1: 2-byte aligned rows (any K): the chunk's 16 bytes start 0 or 2 bytes
+//      into a 4-byte aligned dword; a 16-byte load from there plus the dword
+//      after it, shifted by those 0 or 2 bytes.
+// With G < 8 a chunk can straddle K, and the bytes past K belong to the next
+// row, so the elements past K are masked to zero on their way into LDS.
 template <class C, int ROWS, int WROWS, int G, bool KFULL, int SETS>
 struct KMajorOperand {
     static constexpr bool VEC = G == 8;
-    static constexpr int kUnits = 8 / G;  // loads per 16-byte chunk
-    static_assert(G == 8 || G == 4 || G == 2 || G == 1, "load granularity");
+    static constexpr bool SHIFT = G == 1;
+    static_assert(G == 8 || G == 2 || G == 1, "row alignment");
+    static_assert(VEC || (SETS == 1 && !KFULL), "G < 8: one staging set, K-tiles masked against K");
     static constexpr int RPP = C::kRowsPerPass;
     static constexpr int kPasses = ROWS / RPP;
     static constexpr int kPlane = ROWS * 32 + GEMM_PLANE_PAD;
@@ -369,20 +377,25 @@ struct KMajorOperand {
     static constexpr int kLdsBytes = 2 * kStage;
     static constexpr int kPlanesPerStep = C::MK / 16;
     static_assert(ROWS % RPP == 0, "loader passes");
+    // every pass moves a lane RPP rows on: an even number of rows keeps a
+    // lane's chunks at one offset modulo 4 bytes whatever K is
+    static_assert(RPP % 2 == 0, "rows per pass");
     // WROWS: rows of this operand one wave reads fragments from; the read
     // immediates reach stage + last plane + last fragment of the wave.
     static_assert(kStage + (C::kPlanes - 1) * kPlane + (WROWS - C::MB) * 32 < 65536,
                   "LDS immediates must fit the 16-bit offset field");
 
     int4v regs[SETS][kPasses];
-    uint32_t voff[kPasses];  // G > 1: byte offset of this lane's chunk from the K-tile start
+    uint32_t next[SHIFT ? kPasses : 1];  // G == 1: the dword after each chunk's 16-byte load
+    uint32_t voff[kPasses];  // byte offset of this lane's chunk (G < 8: of its 4-byte aligned start)
     int chunk, row0, k_elems, k_tiles;
-    const _Float16 *tile;
-    uint32_t bytes;
+    const char *tile;  // first row of the block tile (G < 8: rounded down to 4 bytes)
+    uint32_t bytes;    // the block's rows (G < 8: from the rounded-down start, whole dwords)
     __amdgpu_buffer_rsrc_t rsrc0, rsrc_t, rsrc_none;
-    uint32_t mask;               // G == 8: the chunk past K
-    uint32_t umask[kUnits];      // 1 < G < 8: each load unit of the chunk past K
-    uint32_t soff;  // KFULL: byte offset of the K-tile inside each row
+    uint32_t mask;     // G == 8, K % 64 != 0: the chunk past K
+    uint32_t soff;     // KFULL: byte offset of the K-tile inside each row
+    uint32_t shift;    // G == 1: bytes between the dword start and the chunk, 0 or 2
+    int kvalid[2];     // G < 8: elements of the chunk inside K, for the K-tile of each LDS stage
     int k0;
     int w_lane, r_lane;
 
@@ -395,12 +408,30 @@ struct KMajorOperand {
         row0 = tid >> 3;
         k_elems = K;
         k_tiles = kt_count;
-        tile = base;
-        bytes = (uint32_t)rows_valid * (uint32_t)K * 2u;
-        rsrc0 = make_rsrc(base, bytes);
-        rsrc_none = make_rsrc(base, 0u);
+        if constexpr (VEC) {
+            tile = reinterpret_cast<const char *>(base);
+            bytes = (uint32_t)rows_valid * (uint32_t)K * 2u;
 #pragma unroll
-        for (int i = 0; i < kPasses; ++i) voff[i] = (uint32_t)((row0 + RPP * i) * K + chunk * 8) * 2u;
+            for (int i = 0; i < kPasses; ++i) voff[i] = (uint32_t)((row0 + RPP * i) * K + chunk * 8) * 2u;
+        } else {
+            // The descriptor starts at the dword holding the first element
+            // and ends with the dword holding the last one: a dword is read
+            // only when all of it is in range, and a dword that holds an
+            // element lies in the element's page.  Rows past rows_valid get
+            // kOutOfRange: a load only drops bytes past num_records, and the
+            // dword after the block's last element can be the next row's.
+            const uint32_t lead = (uint32_t)((uintptr_t)base & 3u);  // 0, or 2 with G == 1
+            tile = reinterpret_cast<const char *>(base) - lead;
+            bytes = ((uint32_t)rows_valid * (uint32_t)K * 2u + lead + 3u) & ~3u;
+            shift = ((uint32_t)row0 * (uint32_t)K * 2u + lead) & 2u;
+#pragma unroll
+            for (int i = 0; i < kPasses; ++i) {
+                const int row = row0 + RPP * i;
+                voff[i] = row < rows_valid ? (uint32_t)(row * K + chunk * 8) * 2u + lead - shift : kOutOfRange;
+            }
+        }
+        rsrc0 = make_rsrc(tile, bytes);
+        rsrc_none = make_rsrc(tile, 0u);
         w_lane = lds + (chunk >> 1) * kPlane + row0 * 32 + (((chunk & 1) ^ half_swap(row0)) * 16);
         // fragment reads: 32x32x16 lane l takes row l % 32, k half l / 32 of
         // the step's plane; 16x16x32 lane l takes row l % 16, plane 2 ks +
@@ -414,9 +445,11 @@ struct KMajorOperand {
     // KFULL (K % BK == 0, VEC): the block's descriptor for every K-tile,
     // the K-tile's byte offset in soffset, and an empty descriptor for the
     // K-tiles past K.  Otherwise a descriptor per K-tile whose range ends
-    // with the block's last row; chunks past K (K % 8 == 0 on the VEC path,
-    // so a chunk is wholly inside or wholly past K) get kOutOfRange.  Both
-    // read zeros wherever the tile leaves the matrix.
+    // with the block's last row, and reads past the last K-tile get an
+    // empty range.  With G == 8 (K % 8 == 0) a chunk is wholly inside or
+    // wholly past K, and the chunks past K get kOutOfRange; with G < 8 the
+    // store masks each chunk against K.  All of these read zeros wherever
+    // the tile leaves the matrix.
     __device__ __forceinline__ void begin_tile(int t) {
         k0 = t * C::BK;
         if constexpr (VEC && KFULL) {
@@ -426,12 +459,12 @@ struct KMajorOperand {
         } else {
             const uint32_t skip = (uint32_t)t * (C::BK * 2);
             const bool live = t < k_tiles;
-            rsrc_t = make_rsrc(tile + (live ? t * C::BK : 0), (live && bytes > skip) ? bytes - skip : 0u);
+            rsrc_t = make_rsrc(tile + (live ? skip : 0u), (live && bytes > skip) ? bytes - skip : 0u);
             soff = 0;
             mask = (k0 + chunk * 8 >= k_elems) ? kOutOfRange : 0u;
-            // K % G == 0: a unit of G elements is wholly inside or wholly past K
-#pragma unroll
-            for (int u = 0; u < kUnits; ++u) umask[u] = (k0 + chunk * 8 + u * G >= k_elems) ? kOutOfRange : 0u;
+            // With one staging set, K-tile t is stored into LDS stage t % 2,
+            // after begin_tile(t) and before begin_tile(t + 2).
+            if constexpr (!VEC) kvalid[t & 1] = k_elems - (k0 + chunk * 8);
         }
     }
 
@@ -441,38 +474,30 @@ struct KMajorOperand {
                 regs[set][i] = __builtin_amdgcn_raw_buffer_load_b128(rsrc_t, voff[i], soff, 0);
             else
                 regs[set][i] = __builtin_amdgcn_raw_buffer_load_b128(rsrc_t, voff[i] | mask, 0, 0);
-        } else if constexpr (G == 4) {
-            typedef int int2v __attribute__((ext_vector_type(2)));
-            const int2v lo = __builtin_amdgcn_raw_buffer_load_b64(rsrc_t, voff[i] | umask[0], 0, 0);
-            const int2v hi = __builtin_amdgcn_raw_buffer_load_b64(rsrc_t, (voff[i] + 8u) | umask[1], 0, 0);
-            regs[set][i] = int4v{lo[0], lo[1], hi[0], hi[1]};
-        } else if constexpr (G == 2) {
-            int4v r;
-#pragma unroll
-            for (int u = 0; u < 4; ++u)
-                r[u] = __builtin_amdgcn_raw_buffer_load_b32(rsrc_t, (voff[i] + 4u * u) | umask[u], 0, 0);
-            regs[set][i] = r;
         } else {
-            // every element bounds-checked against K; rows past the tile's
-            // valid rows are past num_records
-            const int row = row0 + RPP * i;
-            const int kc = k0 + chunk * 8;
-            union {
-                short s[8];
-                int4v v;
-            } u;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const uint32_t off =
-                    (kc + e < k_elems) ? (uint32_t)(row * k_elems + kc + e) * 2u : kOutOfRange;
-                u.s[e] = __builtin_amdgcn_raw_buffer_load_b16(rsrc0, off, 0, 0);
-            }
-            regs[set][i] = u.v;
+            regs[set][i] = __builtin_amdgcn_raw_buffer_load_b128(rsrc_t, voff[i], 0, 0);
+            if constexpr (SHIFT) next[i] = __builtin_amdgcn_raw_buffer_load_b32(rsrc_t, voff[i] + 16u, 0, 0);
         }
     }
 
     __device__ __forceinline__ void store(char *smem, int i, int stage, int set) const {
-        *reinterpret_cast<int4v *>(smem + w_lane + stage * kStage + i * RPP * 32) = regs[set][i];
+        int4v v = regs[set][i];
+        if constexpr (!VEC) {
+            if constexpr (SHIFT) {
+                const uint32_t w4 = next[i];
+                v = int4v{(int)__builtin_amdgcn_alignbyte((uint32_t)v[1], (uint32_t)v[0], shift),
+                          (int)__builtin_amdgcn_alignbyte((uint32_t)v[2], (uint32_t)v[1], shift),
+                          (int)__builtin_amdgcn_alignbyte((uint32_t)v[3], (uint32_t)v[2], shift),
+                          (int)__builtin_amdgcn_alignbyte(w4, (uint32_t)v[3], shift)};
+            }
+            // element e of the chunk is kept when e < kv (fp16 e sits in
+            // the low half of dword e / 2 when e is even)
+            const int kv = stage ? kvalid[1] : kvalid[0];
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                v[j] &= (kv > 2 * j + 1) ? -1 : (kv > 2 * j) ? 0xffff : 0;
+        }
+        *reinterpret_cast<int4v *>(smem + w_lane + stage * kStage + i * RPP * 32) = v;
     }
 
     __device__ __forceinline__ half8 read(const char *smem, int stage, int ks, int f) const {
@@ -491,6 +516,12 @@ struct KMajorOperand {
 // half-wave fall on disjoint banks.  Each pass covers RPP k-rows; thread t
 // owns 16-byte chunk t % (BN/8) of k-row t / (BN/8) + RPP * i, so
 // consecutive lanes read consecutive n (coalesced).
+// VEC: N % 8 == 0 and a 16-byte aligned B, one 16-byte load per chunk.
+// Otherwise the k-rows are 2-byte aligned: as in KMajorOperand with G == 1,
+// a 16-byte load at the 4-byte aligned offset below the chunk and the dword
+// after it, shifted into place.  The elements of a chunk past N are left as
+// they come (the next k-row's): column n of B reaches only column n of D,
+// and D's columns past N are never stored.  k-rows past K are zeroed.
 template <class C, bool VEC, int SETS>
 struct NMajorB {
     static constexpr int BN = C::BN, BK = C::BK;
@@ -503,11 +534,21 @@ struct NMajorB {
     static_assert(C::MB == 32, "the transposed B path feeds 32x32x16 MFMAs");
     static_assert(C::kThreads % kCpr == 0 && BK % RPP == 0, "loader passes");
     static_assert(15 * kPitch + 4 * kPitch + BN * 2 < 65536, "LDS immediates");
+    static_assert(VEC || SETS == 1, "unaligned rows: one staging set, k-rows masked against K");
+    // an even number of k-rows per pass keeps a lane's chunks at one offset
+    // modulo 4 bytes whatever N is
+    static_assert(RPP % 2 == 0, "rows per pass");
 
     int4v regs[SETS][kPasses];
-    uint32_t voff[kPasses];  // VEC: byte offset from the K-tile's first row; bit 31 set past N
+    uint32_t next[VEC ? 1 : kPasses];  // !VEC: the dword after each chunk's 16-byte load
+    // byte offset from the K-tile's first row (!VEC: of the 4-byte aligned
+    // start); VEC: bit 31 set past N
+    uint32_t voff[kPasses];
     int chunk, row0, n_total, k_elems, k_tiles, n0;
-    const _Float16 *b;
+    const char *b;     // !VEC: rounded down to 4 bytes
+    uint32_t lead;     // bytes b was rounded down by
+    uint32_t shift;    // !VEC: bytes between the dword start and the chunk, 0 or 2
+    int krows[2];      // !VEC: k-rows inside K of the K-tile of each LDS stage
     __amdgpu_buffer_rsrc_t rsrc_t;
     int k0;
     int w_lane, r_lane[2];
@@ -520,11 +561,25 @@ struct NMajorB {
         k_elems = K;
         k_tiles = kt_count;
         n0 = n_first;
-        b = bmat;
-        const uint32_t col_mask = (n0 + chunk * 8 >= N) ? kOutOfRange : 0u;  // N % 8 == 0 on VEC
+        if constexpr (VEC) {
+            lead = 0;
+            const uint32_t col_mask = (n0 + chunk * 8 >= N) ? kOutOfRange : 0u;  // N % 8 == 0
 #pragma unroll
-        for (int i = 0; i < kPasses; ++i)
-            voff[i] = ((uint32_t)((row0 + RPP * i) * N + n0 + chunk * 8) * 2u) | col_mask;
+            for (int i = 0; i < kPasses; ++i)
+                voff[i] = ((uint32_t)((row0 + RPP * i) * N + n0 + chunk * 8) * 2u) | col_mask;
+        } else {
+            // A chunk wholly past N reads the block's first chunk instead:
+            // its columns are never stored.  Then every offset is below
+            // 64 * N * 2 + 20 < 2^32 (N < 2^25), and a multiple of 4: the
+            // chunk's column is a multiple of 8, and RPP is even.
+            lead = (uint32_t)((uintptr_t)bmat & 3u);
+            shift = ((uint32_t)row0 * (uint32_t)N * 2u + lead) & 2u;
+            const int nc = n0 + chunk * 8 < N ? n0 + chunk * 8 : n0;
+#pragma unroll
+            for (int i = 0; i < kPasses; ++i)
+                voff[i] = (uint32_t)((row0 + RPP * i) * N + nc) * 2u + lead - shift;
+        }
+        b = reinterpret_cast<const char *>(bmat) - lead;
         w_lane = lds + row0 * kPitch + chunk * 16;
         const int g = lane >> 4, j = lane & 15;
         const int base = lds + (8 * (lane >> 5) + (j >> 2)) * kPitch + (frag_col + 16 * (g & 1) + 4 * (j & 3)) * 2;
@@ -532,34 +587,37 @@ struct NMajorB {
         r_lane[1] = base + kStage;
     }
 
-    // K-tile t: k-rows t*BK .. ; the range ends at the last k-row inside K.
+    // K-tile t: k-rows t*BK .. ; the range ends at the last k-row inside K
+    // (!VEC: with the dword that holds its last element).
     __device__ __forceinline__ void begin_tile(int t) {
         k0 = t * BK;
         const int rows = t < k_tiles ? min(BK, k_elems - k0) : 0;
-        rsrc_t = make_rsrc(b + (t < k_tiles ? (int64_t)k0 * n_total : 0), (uint32_t)rows * (uint32_t)n_total * 2u);
+        const uint32_t span = (uint32_t)rows * (uint32_t)n_total * 2u;
+        rsrc_t = make_rsrc(b + (t < k_tiles ? (int64_t)k0 * n_total * 2 : 0),
+                           VEC || rows == 0 ? span : (span + lead + 3u) & ~3u);
+        // With one staging set, K-tile t is stored into LDS stage t % 2,
+        // after begin_tile(t) and before begin_tile(t + 2).
+        if constexpr (!VEC) krows[t & 1] = rows;
     }
 
     __device__ __forceinline__ void load(int i, int set) {
-        if constexpr (VEC) {
-            regs[set][i] = __builtin_amdgcn_raw_buffer_load_b128(rsrc_t, voff[i], 0, 0);
-        } else {
-            const int row = row0 + RPP * i;
-            const int nc = n0 + chunk * 8;
-            union {
-                short s[8];
-                int4v v;
-            } u;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const uint32_t off = (nc + e < n_total) ? (uint32_t)(row * n_total + nc + e) * 2u : kOutOfRange;
-                u.s[e] = __builtin_amdgcn_raw_buffer_load_b16(rsrc_t, off, 0, 0);
-            }
-            regs[set][i] = u.v;
-        }
+        regs[set][i] = __builtin_amdgcn_raw_buffer_load_b128(rsrc_t, voff[i], 0, 0);
+        if constexpr (!VEC) next[i] = __builtin_amdgcn_raw_buffer_load_b32(rsrc_t, voff[i] + 16u, 0, 0);
     }
 
     __device__ __forceinline__ void store(char *smem, int i, int stage, int set) const {
-        *reinterpret_cast<int4v *>(smem + w_lane + stage * kStage + i * RPP * kPitch) = regs[set][i];
+        int4v v = regs[set][i];
+        if constexpr (!VEC) {
+            const uint32_t w4 = next[i];
+            v = int4v{(int)__builtin_amdgcn_alignbyte((uint32_t)v[1], (uint32_t)v[0], shift),
+                      (int)__builtin_amdgcn_alignbyte((uint32_t)v[2], (uint32_t)v[1], shift),
+                      (int)__builtin_amdgcn_alignbyte((uint32_t)v[3], (uint32_t)v[2], shift),
+                      (int)__builtin_amdgcn_alignbyte(w4, (uint32_t)v[3], shift)};
+            // a k-row past K can hold the element that shares the last
+            // element's dword: it must not meet A's zeros as a NaN
+            if (row0 + RPP * i >= (stage ? krows[1] : krows[0])) v = int4v{0, 0, 0, 0};
+        }
+        *reinterpret_cast<int4v *>(smem + w_lane + stage * kStage + i * RPP * kPitch) = v;
     }
 
     __device__ __forceinline__ half8 read(const char *smem, int stage, int ks, int f) const {
@@ -757,8 +815,8 @@ constexpr int step_op_index(int o, int nr, int nw) {
 //
 // NN == false: C fp16 [M,N] = A [M,K] * B[N,K]^T (the tutorial's contract).
 // NN == true:  D fp32 [M,N] = A [M,K] * B[K,N]   (the day-78 listing's).
-// G: elements per global load of the K-major operands (8 = the 16-byte
-// path); KFULL: G == 8 and K a multiple of the K-tile (one descriptor per
+// G: row alignment of the K-major operands (8, 2 or 1; KMajorOperand);
+// KFULL: G == 8 and K a multiple of the K-tile (one descriptor per
 // operand).
 template <class C, int G, bool NN, bool KFULL>
 __global__ __launch_bounds__(C::kThreads)
@@ -766,10 +824,10 @@ __attribute__((amdgpu_waves_per_eu(C::kMinWavesPerEU, C::kMinWavesPerEU)))
 void gemm_f16_kernel(const Params p) {
     constexpr int BM = C::BM, BN = C::BN, KS = C::KS;
     constexpr int TM = C::TM, TN = C::TN, FM = C::FM, FN = C::FN, MB = C::MB;
-    // the scalar loader's per-element loads keep too many registers in
-    // flight for a second staging set
+    // with rows not 16-byte aligned the loads and the masks against K keep
+    // too many registers live for a second staging set
     constexpr bool VEC = G == 8;
-    static_assert(!NN || G == 8 || G == 1, "D = A B: 16-byte or per-element loads");
+    static_assert(!NN || G == 8 || G == 1, "D = A B: 16-byte aligned rows, or any");
     constexpr int SETS = VEC ? C::kSets : 1;
     using OpA = KMajorOperand<C, BM, TM, G, KFULL, SETS>;
     using OpB = std::conditional_t<NN, NMajorB<C, VEC, SETS>, KMajorOperand<C, BN, TN, G, KFULL, SETS>>;
@@ -2490,8 +2548,8 @@ inline hipError_t launch_kernel(Kernel kernel, dim3 grid, dim3 block, hipStream_
 }
 
 // Launch of block tile C.  CD: the configuration of the direct-to-LDS kernels
-// (16-byte loads); C: the register-staged kernel's.  g: fp16 elements per
-// global load (8, 4, 2 or 1, from K and the operands' alignment); cus: the
+// (16-byte loads); C: the register-staged kernel's.  g: the operands' row
+// alignment (8: 16 bytes, 2: 4 bytes, 1: 2 bytes; KMajorOperand); cus: the
 // device's compute units (0 if unknown: no one-workgroup-per-CU kernel).
 // The 256x256 register-staged kernels exist only for 16-byte loads: with
 // narrower ones their staging registers spill, so the host runs those
@@ -2555,7 +2613,6 @@ hipError_t launch(const Params &p, int g, int cus, hipStream_t stream) {
     }
     if constexpr (!(C::BM == 256 && C::BN == 256)) {
         if constexpr (!NN) {
-            if (g == 4) return launch_kernel(gemm_f16_kernel<C, 4, NN, false>, grid, block, stream, p);
             if (g == 2) return launch_kernel(gemm_f16_kernel<C, 2, NN, false>, grid, block, stream, p);
         }
         return launch_kernel(gemm_f16_kernel<C, 1, NN, false>, grid, block, stream, p);

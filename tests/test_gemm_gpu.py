@@ -39,12 +39,14 @@ def _announce(*what):
 
 def run_gemm(a_np, b_np, a_offset=0, b_offset=0, **opts):
     """C from the HIP path; A/B may be placed `offset` elements past an aligned
-    base to exercise the unaligned loader.  C sits between guard bands."""
+    base to exercise the unaligned loader.  The elements around A and B are
+    NaN, so a kernel that let one of them into a product would show it.  C
+    sits between guard bands."""
     m, k = a_np.shape
     n = b_np.shape[0]
     dev = torch.device("cuda")
-    a_buf = torch.zeros(a_offset + m * k + 8, dtype=torch.float16, device=dev)
-    b_buf = torch.zeros(b_offset + n * k + 8, dtype=torch.float16, device=dev)
+    a_buf = torch.full((a_offset + m * k + 8,), float("nan"), dtype=torch.float16, device=dev)
+    b_buf = torch.full((b_offset + n * k + 8,), float("nan"), dtype=torch.float16, device=dev)
     if m * k:
         a_buf[a_offset:a_offset + m * k] = torch.from_numpy(a_np.reshape(-1)).to(dev)
     if n * k:
@@ -161,15 +163,21 @@ def test_ragged_shapes(m, n, k, tile):
     assert_ulp(run_gemm(a, b, tile=tile), oracle.gemm_f16_nt(a, b), k, f"{m}x{n}x{k}")
 
 
-# K and operand offsets (in elements) chosen so each global-load width runs:
-# 8-byte loads (K % 4 == 0 and rows 8-byte aligned), 4-byte loads (K % 2 == 0
-# and rows 4-byte aligned) and one element per load (odd K).
+# K and operand offsets (in elements) chosen so each row alignment of the
+# register-staged loader runs: 4-byte aligned rows (K even, operands 4-byte
+# aligned), whose 16-byte loads start at 4-byte aligned offsets, and 2-byte
+# aligned rows (odd K: every other row; an operand at an odd element offset:
+# every row), whose loads are shifted by 2 bytes.  Chunks straddle K in the
+# last K-tile, and below one K-tile.
 GRANULARITY = [
-    (100, 0, 0), (132, 0, 0), (2500, 0, 0), (4, 0, 0),  # K % 8 == 4: 8-byte loads
-    (98, 0, 0), (130, 0, 0), (6, 0, 0), (1026, 0, 0),   # K % 4 == 2: 4-byte loads
+    (100, 0, 0), (132, 0, 0), (2500, 0, 0), (4, 0, 0),  # K % 8 == 4
+    (98, 0, 0), (130, 0, 0), (6, 0, 0), (1026, 0, 0),   # K % 8 == 2 or 6
     (96, 4, 0), (96, 0, 4),                             # K % 8 == 0, an operand 8-byte aligned
     (96, 2, 0), (64, 0, 6),                             # ... an operand 4-byte aligned
-    (99, 0, 0),                                         # odd K: one element per load
+    (99, 0, 0), (1, 0, 0), (7, 0, 0), (63, 0, 0),       # odd K
+    (65, 0, 0), (129, 0, 0), (1001, 0, 0),
+    (96, 1, 0), (64, 0, 3), (98, 1, 1),                 # even K, an operand at an odd offset
+    (99, 1, 0), (101, 0, 5), (127, 3, 7),               # odd K and odd offsets
 ]
 
 
@@ -447,7 +455,7 @@ def test_hip_graph_capture_and_replay():
 
 
 @pytest.mark.parametrize("a_off,b_off", [(1, 0), (0, 3), (5, 7)])
-def test_unaligned_operands_take_the_scalar_loader(a_off, b_off):
+def test_unaligned_operands_take_the_register_staged_loader(a_off, b_off):
     _announce("unaligned", a_off, b_off)
     rng = np.random.default_rng(a_off * 10 + b_off)
     m, n, k = 150, 140, 96

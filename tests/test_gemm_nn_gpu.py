@@ -46,8 +46,9 @@ def run_nn(a_np, b_np, a_offset=0, b_offset=0, **opts):
     kb, n = b_np.shape
     assert kb == k
     dev = torch.device("cuda")
-    a_buf = torch.zeros(a_offset + m * k + 8, dtype=torch.float16, device=dev)
-    b_buf = torch.zeros(b_offset + k * n + 8, dtype=torch.float16, device=dev)
+    # NaN around A and B: an element outside them in a product would show
+    a_buf = torch.full((a_offset + m * k + 8,), float("nan"), dtype=torch.float16, device=dev)
+    b_buf = torch.full((b_offset + k * n + 8,), float("nan"), dtype=torch.float16, device=dev)
     if m * k:
         a_buf[a_offset:a_offset + m * k] = torch.from_numpy(a_np.reshape(-1)).to(dev)
     if k * n:
@@ -164,8 +165,9 @@ def test_persistent_path_bit_exact(tile, m, n, k):
     assert_exact(run_nn(a, b, tile=tile), d64, f"{m}x{n}x{k}")
 
 
-@pytest.mark.parametrize("m,n,k", [(70, 13, 40), (33, 100, 24), (64, 21, 19)])
-def test_n_or_k_not_multiple_of_8_takes_the_scalar_loaders(m, n, k):
+@pytest.mark.parametrize("m,n,k", [(70, 13, 40), (33, 100, 24), (64, 21, 19), (150, 140, 99), (130, 70, 129),
+                                   (300, 40, 1001)])
+def test_n_or_k_not_multiple_of_8_takes_the_register_staged_loaders(m, n, k):
     _announce("nn scalar", m, n, k)
     rng = np.random.default_rng(n * k)
     a = (rng.integers(-8, 9, size=(m, k)) / 8).astype(np.float16)
