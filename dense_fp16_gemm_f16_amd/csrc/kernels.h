@@ -152,6 +152,11 @@ constexpr uint32_t kOutOfRange = 0x80000000u;  // buffer offset past any num_rec
 #ifndef GEMM_STREAM_NT
 #define GEMM_STREAM_NT 1
 #endif
+// 1: the stream kernel also serves K % 64 != 0 (a partial last K-tile per
+// tile); 0: those shapes take one workgroup per tile
+#ifndef GEMM_STREAM_PARTIAL_K
+#define GEMM_STREAM_PARTIAL_K 1
+#endif
 // sixteenths of a K-tile's loads issued in step 0 (the rest in step 1)
 #ifndef GEMM_AHEAD_STEP0_LOADS
 #define GEMM_AHEAD_STEP0_LOADS 10
@@ -1964,7 +1969,9 @@ __device__ __forceinline__ void mfma16_first(half8 a, half8 b, floatx4 &c) {
 // that K-tile leaves the U stores in flight and the next K-tile's waits for
 // them.  The last tile stores its units after the loop.  POL: the stores'
 // cache policy (CStore), chosen by the host, so no store is behind a branch.
-template <class C, int POL>
+// KFULL: K a multiple of the K-tile; otherwise the chunks of every tile's
+// last K-tile that lie past K get an out-of-range offset and read as zeros.
+template <class C, int POL, bool KFULL = true>
 __global__ __launch_bounds__(C::kThreads)
 __attribute__((amdgpu_waves_per_eu(C::kMinWavesPerEU, C::kMinWavesPerEU)))
 void gemm_f16_stream_kernel(const Params p) {
@@ -1972,8 +1979,8 @@ void gemm_f16_stream_kernel(const Params p) {
     constexpr int TM = C::TM, TN = C::TN, FM = C::FM, FN = C::FN;
     static_assert(C::MB == 16 && C::KS == 2, "two 32-wide k steps per K-tile");
     static_assert(FN % 2 == 0, "B fragments in pairs");
-    using OpA = KMajorDirect<C, BM, true>;
-    using OpB = KMajorDirect<C, BN, true, true>;
+    using OpA = KMajorDirect<C, BM, KFULL>;
+    using OpB = KMajorDirect<C, BN, KFULL, true>;
     constexpr int kLdsB = OpA::kLdsBytes;
     constexpr int kLds = OpA::kLdsBytes + OpB::kLdsBytes;
     constexpr int LA = OpA::kLoads, L = OpA::kLoads + OpB::kLoads;
@@ -1993,7 +2000,11 @@ void gemm_f16_stream_kernel(const Params p) {
     const int wm = wave / C::WN;
     const int wn = wave % C::WN;
 
-    const int kt_count = p.k_tiles;  // even, >= 4 (the host's condition)
+    // K-tiles per tile: even and >= 4.  !KFULL rounds an odd count up: the
+    // extra K-tile lies wholly past K and reads zeros, and its MFMAs add +0
+    // to accumulators that are never -0 (they start at +0), which leaves
+    // every bit unchanged.
+    const int kt_count = KFULL ? p.k_tiles : (p.k_tiles + 1) & ~1;
     const int ntiles = p.num_m * p.num_n;
     const int G = gridDim.x;
     int idx = blockIdx.x;
@@ -2547,6 +2558,17 @@ inline hipError_t launch_kernel(Kernel kernel, dim3 grid, dim3 block, hipStream_
     return hipLaunchKernel(reinterpret_cast<const void *>(kernel), grid, block, args, 0, stream);
 }
 
+// The stream kernel with the host's C store policy: the policy is a
+// template argument, so no store sits behind a branch.
+template <class CD, bool KFULL>
+inline hipError_t launch_stream(const Params &p, dim3 grid, dim3 block, hipStream_t stream) {
+    if (p.c_store == kStoreDevice)
+        return launch_kernel(gemm_f16_stream_kernel<CD, kStoreDevice, KFULL>, grid, block, stream, p);
+    if (p.c_store == kStoreStream && GEMM_STREAM_NT)
+        return launch_kernel(gemm_f16_stream_kernel<CD, kStoreStream, KFULL>, grid, block, stream, p);
+    return launch_kernel(gemm_f16_stream_kernel<CD, kStoreDefault, KFULL>, grid, block, stream, p);
+}
+
 // Launch of block tile C.  CD: the configuration of the direct-to-LDS kernels
 // (16-byte loads); C: the register-staged kernel's.  g: the operands' row
 // alignment (8: 16 bytes, 2: 4 bytes, 1: 2 bytes; KMajorOperand); cus: the
@@ -2577,18 +2599,20 @@ hipError_t launch(const Params &p, int g, int cus, hipStream_t stream) {
             const dim3 block(CD::kThreads);
             if constexpr (GEMM_AHEAD && CD::MB == 16) {
                 // more tiles than CUs: one workgroup per CU walking several
-                // tiles, where its conditions hold
-                if (GEMM_PERSIST && full && p.k_tiles % 2 == 0 && p.k_tiles >= 4 && cus > 0 && tiles > cus &&
-                    p.n % 8 == 0 && ((uintptr_t)p.c % 16) == 0 && (int64_t)CD::BM * p.n * 2 < (int64_t(1) << 31)) {
-                    if constexpr (GEMM_STREAM && CD::FM * CD::FN >= 16) {
-                        // the C store policy is a template argument: no store
-                        // sits behind a branch
+                // tiles, where its conditions hold (the stream kernel also
+                // takes a partial last K-tile)
+                constexpr bool kStream = GEMM_STREAM && CD::FM * CD::FN >= 16;
+                // an even count of at least 4 whole K-tiles; the stream
+                // kernel's KFULL = false copy also takes a partial last
+                // K-tile, and an odd count of at least 3 (rounded up)
+                const bool whole = full && p.k_tiles % 2 == 0 && p.k_tiles >= 4;
+                const bool partial = kStream && GEMM_STREAM_PARTIAL_K && p.k_tiles >= 3;
+                if (GEMM_PERSIST && (whole || partial) && cus > 0 && tiles > cus && p.n % 8 == 0 &&
+                    ((uintptr_t)p.c % 16) == 0 && (int64_t)CD::BM * p.n * 2 < (int64_t(1) << 31)) {
+                    if constexpr (kStream) {
                         const dim3 g1((unsigned)cus);
-                        if (p.c_store == kStoreDevice)
-                            return launch_kernel(gemm_f16_stream_kernel<CD, kStoreDevice>, g1, block, stream, p);
-                        if (p.c_store == kStoreStream && GEMM_STREAM_NT)
-                            return launch_kernel(gemm_f16_stream_kernel<CD, kStoreStream>, g1, block, stream, p);
-                        return launch_kernel(gemm_f16_stream_kernel<CD, kStoreDefault>, g1, block, stream, p);
+                        return whole ? launch_stream<CD, true>(p, g1, block, stream)
+                                     : launch_stream<CD, false>(p, g1, block, stream);
                     }
                     else
                         return launch_kernel(gemm_f16_persistent_kernel<CD, false>, dim3((unsigned)cus), block, stream,

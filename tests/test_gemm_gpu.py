@@ -224,7 +224,14 @@ PERSISTENT = [(g.TILE_64x64, 1100, 1064, 256), (g.TILE_64x64, 2100, 2104, 256),
               (g.TILE_256x128, 4200, 2088, 256), (g.TILE_128x256, 2100, 4152, 256),
               (g.TILE_256x256, 4200, 4096, 512), (g.TILE_128x128, 2100, 2112, 256),
               (g.TILE_256x256, 8200, 2056, 384), (g.TILE_256x128, 4100, 4104, 640),
-              (g.TILE_64x128, 1100, 2104, 256), (g.TILE_128x64, 2100, 1064, 384)]
+              (g.TILE_64x128, 1100, 2104, 256), (g.TILE_128x64, 2100, 1064, 384),
+              # K % 64 != 0: every tile's last K-tile is partial (8, 8, 40 and
+              # 56 of its 64 k), its chunks past K read as zeros
+              (g.TILE_128x128, 2100, 2088, 200), (g.TILE_256x256, 4200, 4152, 456),
+              (g.TILE_256x128, 4200, 2088, 1000), (g.TILE_128x256, 2100, 4152, 248),
+              # an odd K-tile count (15 whole, 3 with a partial last one): the
+              # stream kernel adds a K-tile of zeros
+              (g.TILE_256x128, 4200, 2088, 960), (g.TILE_128x128, 2100, 2088, 136)]
 
 
 @pytest.mark.parametrize("tile,m,n,k", PERSISTENT)
