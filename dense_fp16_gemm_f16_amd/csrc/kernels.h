@@ -419,12 +419,13 @@ struct KMajorOperand {
 #pragma unroll
             for (int i = 0; i < kPasses; ++i) voff[i] = (uint32_t)((row0 + RPP * i) * K + chunk * 8) * 2u;
         } else {
-            // The descriptor starts at the dword holding the first element
-            // and ends with the dword holding the last one: a dword is read
-            // only when all of it is in range, and a dword that holds an
-            // element lies in the element's page.  Rows past rows_valid get
-            // kOutOfRange: a load only drops bytes past num_records, and the
-            // dword after the block's last element can be the next row's.
+            // The descriptor starts at the dword holding the block's first
+            // element and ends with the dword holding its last one: a load
+            // returns a dword only when all 4 of its bytes are in range, and
+            // the dword holding an element lies in that element's page, so
+            // the 2 bytes past the matrix it may hold are mapped.  Rows past
+            // rows_valid get kOutOfRange and read zeros, as on the other
+            // paths.
             const uint32_t lead = (uint32_t)((uintptr_t)base & 3u);  // 0, or 2 with G == 1
             tile = reinterpret_cast<const char *>(base) - lead;
             bytes = ((uint32_t)rows_valid * (uint32_t)K * 2u + lead + 3u) & ~3u;
