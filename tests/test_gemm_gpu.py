@@ -495,6 +495,21 @@ def test_a_sum_of_zeros_is_positive_zero(tile):
     assert_bits_equal(got, oracle.gemm_f16_nt(a, b), "signed zero")
 
 
+# more tiles than CUs: one workgroup per CU walks tiles; an odd K-tile count
+# (3, 15) has a K-tile of zeros added, and K % 64 != 0 a partial last one
+@pytest.mark.parametrize("tile,m,n,k", [(g.TILE_128x128, 2100, 2088, 136), (g.TILE_256x256, 4200, 4152, 960),
+                                        (g.TILE_256x128, 4200, 2088, 1000)])
+def test_a_sum_of_zeros_is_positive_zero_on_the_stream_kernel(tile, m, n, k):
+    """The same sum of -0 products over several tiles per CU: C stays +0."""
+    _announce("signed zero, stream", tile, m, n, k)
+    a = np.zeros((m, k), np.float16)
+    a[:, 0] = 1
+    b = -np.abs(np.random.default_rng(k).standard_normal((n, k))).astype(np.float16)
+    b[:, 0] = -0.0
+    got = run_gemm(a, b, tile=tile)
+    assert np.all(got.view(np.uint16) == 0), "C must be +0"
+
+
 def test_schedule_options_do_not_change_bits():
     """Rasterization only reorders tiles; each output's sum order is fixed."""
     _announce("determinism")
