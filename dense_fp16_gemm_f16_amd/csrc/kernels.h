@@ -152,10 +152,11 @@ constexpr uint32_t kOutOfRange = 0x80000000u;  // buffer offset past any num_rec
 #ifndef GEMM_STREAM_NT
 #define GEMM_STREAM_NT 1
 #endif
-// 1: the stream kernel also serves K % 64 != 0 (a partial last K-tile per
-// tile); 0: those shapes take one workgroup per tile
-#ifndef GEMM_STREAM_PARTIAL_K
-#define GEMM_STREAM_PARTIAL_K 1
+// 1: the one-workgroup-per-CU kernels (stream, persistent) also serve
+// K % 64 != 0 (a partial last K-tile per tile) and an odd K-tile count;
+// 0: those shapes take one workgroup per tile
+#ifndef GEMM_PARTIAL_K
+#define GEMM_PARTIAL_K 1
 #endif
 // sixteenths of a K-tile's loads issued in step 0 (the rest in step 1)
 #ifndef GEMM_AHEAD_STEP0_LOADS
@@ -1232,13 +1233,18 @@ struct NMajorDirect {
     // an opaque copy of the LDS base (see KMajorDirect::refresh_lds)
     __device__ __forceinline__ void refresh_lds() { asm volatile("" : "+s"(lds_w)); }
 
-    // load i of K-tile t (whole: K % BK == 0) of the tile whose columns
-    // start at tile_b = B + tile_n0; bytes: the range of a K-tile from there
-    // (0: the loads read zeros).  The offsets were masked for columns past N
+    // load i of K-tile t of the tile whose columns start at tile_b = B +
+    // tile_n0; bytes: the range of a whole K-tile from there (0: the loads
+    // read zeros).  !KFULL: the range ends with the k-rows inside K (none
+    // past the last K-tile).  The offsets were masked for columns past N
     // from column 0 in init; this adds the tile's own mask.
     template <int S>
     __device__ __forceinline__ void load_tile(char *smem, const _Float16 *tile_b, int tile_n0, uint32_t bytes, int t,
                                               int i) const {
+        if constexpr (!KFULL) {
+            const int rows = min(BK, k_elems - t * BK);
+            bytes = bytes != 0u && rows > 0 ? (uint32_t)(rows * n_total - tile_n0) * 2u : 0u;
+        }
         const uint32_t vo = voff[i] | ((tile_n0 + ccol[i & 1] >= n_total) ? kOutOfRange : 0u);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             make_rsrc(tile_b + (int64_t)t * BK * n_total, bytes),
@@ -1638,9 +1644,11 @@ void gemm_f16_direct_ahead_kernel(const Params p) {
 }
 
 // The fragment-ahead kernel with one workgroup per CU walking several tiles
-// (blockIdx.x, + gridDim.x, ...), for K a multiple of the K-tile with at
-// least 4 (and an even number of) K-tiles, and C with N % 8
-// == 0 and a 16-byte aligned base; NN: B [K,N] and D fp32.  The K-tile stream runs on across tiles:
+// (blockIdx.x, + gridDim.x, ...), for at least 3 K-tiles, and C with N % 8
+// == 0 and a 16-byte aligned base; NN: B [K,N] and D fp32.  KFULL: K a
+// multiple of the K-tile with an even count; otherwise the chunks past K
+// read zeros and an odd count is rounded up by a K-tile of zeros (as in
+// gemm_f16_stream_kernel).  The K-tile stream runs on across tiles:
 // the last two K-tiles of a tile load the next tile's K-tiles 0 and 1 as
 // their "K-tile t+2"; the last one reads no fragments ahead.  Each wave then
 // stages its C through its share of the LDS beyond the two stages and stores
@@ -1650,15 +1658,15 @@ void gemm_f16_direct_ahead_kernel(const Params p) {
 // waits that follow (K-tile 0 before its fragment reads, K-tile 1 at the next
 // tile's first acquire barrier) can leave them in flight (the wait counter
 // is in order): the store burst drains under the next tile's MFMAs.
-template <class C, bool NN>
+template <class C, bool NN, bool KFULL = true>
 __global__ __launch_bounds__(C::kThreads)
 __attribute__((amdgpu_waves_per_eu(C::kMinWavesPerEU, C::kMinWavesPerEU)))
 void gemm_f16_persistent_kernel(const Params p) {
     constexpr int BM = C::BM, BN = C::BN;
     constexpr int TM = C::TM, TN = C::TN, FM = C::FM, FN = C::FN;
     static_assert(C::MB == 16 && C::KS == 2, "two 32-wide k steps per K-tile");
-    using OpA = KMajorDirect<C, BM, true>;
-    using OpB = std::conditional_t<NN, NMajorDirect<C, true>, KMajorDirect<C, BN, true>>;
+    using OpA = KMajorDirect<C, BM, KFULL>;
+    using OpB = std::conditional_t<NN, NMajorDirect<C, KFULL>, KMajorDirect<C, BN, KFULL>>;
     constexpr int kLdsB = OpA::kLdsBytes;
     constexpr int kLds = OpA::kLdsBytes + OpB::kLdsBytes;
     constexpr int LA = OpA::kLoads, L = OpA::kLoads + OpB::kLoads;
@@ -1686,7 +1694,8 @@ void gemm_f16_persistent_kernel(const Params p) {
     const int wm = wave / C::WN;
     const int wn = wave % C::WN;
 
-    const int kt_count = p.k_tiles;  // even, >= 4 (the host's condition)
+    // K-tiles per tile: even and >= 4 (an odd count rounded up, !KFULL)
+    const int kt_count = KFULL ? p.k_tiles : (p.k_tiles + 1) & ~1;
     const int ntiles = p.num_m * p.num_n;
     const int G = gridDim.x;
     int idx = blockIdx.x;
@@ -2588,9 +2597,16 @@ hipError_t launch(const Params &p, int g, int cus, hipStream_t stream) {
         // byte offsets below 2^31
         if (g == 8 && (int64_t)CD::BK * p.n * 2 < (int64_t(1) << 31)) {
             const dim3 block(CD::kThreads);
-            if (GEMM_PERSIST && full && p.k_tiles % 2 == 0 && p.k_tiles >= 4 && cus > 0 && tiles > cus &&
-                ((uintptr_t)p.c % 16) == 0 && (int64_t)CD::BM * p.n * 4 < (int64_t(1) << 31))
-                return launch_kernel(gemm_f16_persistent_kernel<CD, true>, dim3((unsigned)cus), block, stream, p);
+            // an even count of at least 4 whole K-tiles, or (KFULL = false)
+            // at least 3 K-tiles of any kind
+            const bool whole = full && p.k_tiles % 2 == 0 && p.k_tiles >= 4;
+            const bool partial = GEMM_PARTIAL_K && p.k_tiles >= 3;
+            if (GEMM_PERSIST && (whole || partial) && cus > 0 && tiles > cus && ((uintptr_t)p.c % 16) == 0 &&
+                (int64_t)CD::BM * p.n * 4 < (int64_t(1) << 31))
+                return whole ? launch_kernel(gemm_f16_persistent_kernel<CD, true, true>, dim3((unsigned)cus), block,
+                                             stream, p)
+                             : launch_kernel(gemm_f16_persistent_kernel<CD, true, false>, dim3((unsigned)cus), block,
+                                             stream, p);
             return full ? launch_kernel(gemm_f16_direct_ahead_kernel<CD, true, true>, grid, block, stream, p)
                         : launch_kernel(gemm_f16_direct_ahead_kernel<CD, false, true>, grid, block, stream, p);
         }
@@ -2603,21 +2619,21 @@ hipError_t launch(const Params &p, int g, int cus, hipStream_t stream) {
                 // tiles, where its conditions hold (the stream kernel also
                 // takes a partial last K-tile)
                 constexpr bool kStream = GEMM_STREAM && CD::FM * CD::FN >= 16;
-                // an even count of at least 4 whole K-tiles; the stream
-                // kernel's KFULL = false copy also takes a partial last
-                // K-tile, and an odd count of at least 3 (rounded up)
+                // an even count of at least 4 whole K-tiles; the KFULL =
+                // false copies also take a partial last K-tile, and an odd
+                // count of at least 3 (rounded up)
                 const bool whole = full && p.k_tiles % 2 == 0 && p.k_tiles >= 4;
-                const bool partial = kStream && GEMM_STREAM_PARTIAL_K && p.k_tiles >= 3;
+                const bool partial = GEMM_PARTIAL_K && p.k_tiles >= 3;
                 if (GEMM_PERSIST && (whole || partial) && cus > 0 && tiles > cus && p.n % 8 == 0 &&
                     ((uintptr_t)p.c % 16) == 0 && (int64_t)CD::BM * p.n * 2 < (int64_t(1) << 31)) {
-                    if constexpr (kStream) {
-                        const dim3 g1((unsigned)cus);
+                    const dim3 g1((unsigned)cus);
+                    if constexpr (kStream)
                         return whole ? launch_stream<CD, true>(p, g1, block, stream)
                                      : launch_stream<CD, false>(p, g1, block, stream);
-                    }
                     else
-                        return launch_kernel(gemm_f16_persistent_kernel<CD, false>, dim3((unsigned)cus), block, stream,
-                                             p);
+                        return whole ? launch_kernel(gemm_f16_persistent_kernel<CD, false, true>, g1, block, stream, p)
+                                     : launch_kernel(gemm_f16_persistent_kernel<CD, false, false>, g1, block, stream,
+                                                     p);
                 }
                 return full ? launch_kernel(gemm_f16_direct_ahead_kernel<CD, true, false>, grid, block, stream, p)
                             : launch_kernel(gemm_f16_direct_ahead_kernel<CD, false, false>, grid, block, stream, p);

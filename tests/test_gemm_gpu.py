@@ -230,8 +230,11 @@ PERSISTENT = [(g.TILE_64x64, 1100, 1064, 256), (g.TILE_64x64, 2100, 2104, 256),
               (g.TILE_128x128, 2100, 2088, 200), (g.TILE_256x256, 4200, 4152, 456),
               (g.TILE_256x128, 4200, 2088, 1000), (g.TILE_128x256, 2100, 4152, 248),
               # an odd K-tile count (15 whole, 3 with a partial last one): the
-              # stream kernel adds a K-tile of zeros
-              (g.TILE_256x128, 4200, 2088, 960), (g.TILE_128x128, 2100, 2088, 136)]
+              # kernel adds a K-tile of zeros
+              (g.TILE_256x128, 4200, 2088, 960), (g.TILE_128x128, 2100, 2088, 136),
+              # the same on the persistent kernel's tiles
+              (g.TILE_64x64, 1100, 1064, 200), (g.TILE_64x128, 1100, 2104, 136),
+              (g.TILE_128x64, 2100, 1064, 960)]
 
 
 @pytest.mark.parametrize("tile,m,n,k", PERSISTENT)

@@ -152,7 +152,12 @@ def test_direct_to_lds_b_path_bit_exact(m, n, k, tile):
 NN_PERSISTENT = [(g.TILE_128x128, 2100, 2088, 384), (g.TILE_256x256, 4200, 4152, 512),
                  (g.TILE_256x128, 4200, 2088, 256), (g.TILE_128x256, 2100, 4152, 256),
                  (g.TILE_256x256, 4200, 4128, 256), (g.TILE_128x256, 2100, 4160, 256),
-                 (g.TILE_64x128, 1100, 2104, 256)]
+                 (g.TILE_64x128, 1100, 2104, 256),
+                 # K % 64 != 0 (a partial last K-tile) and odd K-tile counts
+                 # (a K-tile of zeros added)
+                 (g.TILE_128x128, 2100, 2088, 200), (g.TILE_256x128, 4200, 2088, 1000),
+                 (g.TILE_128x256, 2100, 4152, 248), (g.TILE_256x128, 4200, 2088, 960),
+                 (g.TILE_64x128, 1100, 2104, 136)]
 
 
 @pytest.mark.parametrize("tile,m,n,k", NN_PERSISTENT)
