@@ -67,7 +67,7 @@ enum {
  * [M,N] are never written.
  * Speed: K % 8 == 0 with 16-byte aligned A and B loads the operands straight
  * into LDS; any other K or alignment goes through registers, at roughly
- * 0.55-0.7 of that speed on large shapes.  The result is the same either way.
+ * 0.55-0.7 of that speed on large shapes.
  */
 int gemm_f16_nt(int64_t m, int64_t n, int64_t k, const void *a, const void *b,
                 void *c, void *stream);
