@@ -147,6 +147,22 @@ def test_large_workloads_whole_c(name):
     assert_ulp(got, oracle.gemm_f16_nt(a, b), w.k, name)
 
 
+# K % 64 != 0 and an odd K-tile count at full size, on random operands: the
+# one-workgroup-per-CU kernels with a partial last K-tile (1000: 16 K-tiles,
+# the last 40 k; 960: 15) and a K-tile of zeros added (960).  Rows of C
+# sampled across every 256-row block, checked element by element.
+@pytest.mark.parametrize("m,n,k", [(8192, 8192, 1000), (8192, 8192, 960), (16384, 4096, 2000)])
+def test_partial_k_tiles_at_full_size(m, n, k):
+    _announce("partial K, full size", m, n, k)
+    rng = np.random.default_rng(m + n + k)
+    a = rng.uniform(-1, 1, size=(m, k)).astype(np.float16)
+    b = rng.uniform(-1, 1, size=(n, k)).astype(np.float16)
+    got = run_gemm(a, b)
+    rows = np.arange(m // 256) * 256 + rng.integers(0, 256, size=m // 256)
+    ref = oracle.gemm_f16_nt_rows(a, b, rows)
+    assert_ulp(got[rows], ref, k, f"{m}x{n}x{k} sampled rows")
+
+
 RAGGED = [
     (1, 1, 1), (1, 1, 8), (7, 5, 3), (31, 33, 17), (33, 31, 64), (64, 64, 64), (65, 63, 72),
     (129, 200, 136), (255, 257, 1000), (257, 255, 520), (300, 70, 7), (513, 130, 65),
