@@ -147,6 +147,22 @@ def test_large_workloads_whole_c(name):
     assert_ulp(got, oracle.gemm_f16_nt(a, b), w.k, name)
 
 
+# Rows that are not 16-byte aligned at full size, on random operands: the
+# register-staged loaders with 16-byte loads at 4-byte aligned offsets (K
+# even) and shifted by 2 bytes (odd K, or A at an odd element offset).  Rows
+# of C sampled across every 256-row block, checked element by element.
+@pytest.mark.parametrize("m,n,k,a_off", [(4096, 4096, 4095, 0), (4096, 4096, 4094, 0), (4096, 4096, 4096, 1)])
+def test_unaligned_rows_at_full_size(m, n, k, a_off):
+    _announce("unaligned rows, full size", m, n, k, a_off)
+    rng = np.random.default_rng(m + n + k + a_off)
+    a = rng.uniform(-1, 1, size=(m, k)).astype(np.float16)
+    b = rng.uniform(-1, 1, size=(n, k)).astype(np.float16)
+    got = run_gemm(a, b, a_offset=a_off)
+    rows = np.arange(m // 256) * 256 + rng.integers(0, 256, size=m // 256)
+    ref = oracle.gemm_f16_nt_rows(a, b, rows)
+    assert_ulp(got[rows], ref, k, f"{m}x{n}x{k} A offset {a_off} sampled rows")
+
+
 # K % 64 != 0 and an odd K-tile count at full size, on random operands: the
 # one-workgroup-per-CU kernels with a partial last K-tile (1000: 16 K-tiles,
 # the last 40 k; 960: 15) and a K-tile of zeros added (960).  Rows of C
