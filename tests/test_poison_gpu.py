@@ -78,7 +78,11 @@ def test_direct_paths_every_tile(tile, k):
 
 @pytest.mark.parametrize("tile,m,n,k", [(g.TILE_256x256, 4608, 4096, 256), (g.TILE_128x128, 2100, 2112, 1024),
                                         (g.TILE_256x128, 4100, 4104, 640), (g.TILE_64x64, 1100, 1064, 256),
-                                        (g.TILE_64x128, 1100, 2104, 256)])
+                                        (g.TILE_64x128, 1100, 2104, 256),
+                                        # a partial last K-tile, and an odd count
+                                        # (a K-tile of zeros added)
+                                        (g.TILE_256x256, 4608, 4096, 456), (g.TILE_128x128, 2100, 2112, 136),
+                                        (g.TILE_64x64, 1100, 1064, 200), (g.TILE_256x128, 4100, 4104, 960)])
 def test_one_workgroup_per_cu(tile, m, n, k):
     rng = np.random.default_rng(m + n + k)
     _check_nt(_eighths(rng, (m, k)), _eighths(rng, (n, k)), f"per-CU tile {tile} {m}x{n}x{k}", tile=tile)
@@ -101,7 +105,8 @@ def test_variants(variant):
 
 
 @pytest.mark.parametrize("m,n,k,tile", [(300, 520, 640, g.TILE_AUTO), (300, 520, 1000, g.TILE_128x128),
-                                        (4608, 4096, 256, g.TILE_256x256), (300, 524, 1001, g.TILE_AUTO)])
+                                        (4608, 4096, 256, g.TILE_256x256), (300, 524, 1001, g.TILE_AUTO),
+                                        (4608, 4096, 456, g.TILE_256x256), (2100, 2112, 136, g.TILE_128x128)])
 def test_second_contract(m, n, k, tile):
     rng = np.random.default_rng(m * n + k)
     a, b = _eighths(rng, (m, k)), _eighths(rng, (k, n))
