@@ -9,9 +9,12 @@ Timing follows the tutorials' protocol (CUDA-event timed, median of three
 fresh processes, "4. Pipeline Abstraction and Two Consumer Warp Groups",
 section "Performance").  This process never touches the GPU: it draws the
 inputs of every workload once, then starts --procs fresh child processes one
-after another.  Each child first times each of the five workloads (5
-warm-up launches, then 50 event-timed ones, 200 for the launch-bound
-256^3), then, for the headline workload, runs W untimed warm-up GEMMs and
+after another.  Each child first times each of the five workloads: warm-up
+launches back to back for at least --config-warmup seconds (at least 5;
+the clock takes milliseconds to settle after the load changes, and 0.1 s
+and 0.3 s give the same figures), then 50 event-timed launches, 200 for the
+launch-bound 256^3.  Then, for the headline workload, it runs W untimed
+warm-up GEMMs and
 exactly K timed GEMMs between two device synchronisations, every launch
 also bracketed by HIP events on the stream it runs on (the kernel's average
 duration, for the roofline figure); then a sustained run of back-to-back
@@ -179,11 +182,20 @@ def child(args) -> int:
         wall, durs = headline_steps()
         out["cold_start"] = {"wall_s": wall, "kernel_us": durs}
 
-    # every workload: 5 warm-up launches, then 50 (256^3: 200) event-timed
+    # every workload: warm-up launches back to back for at least
+    # --config-warmup seconds (at least 5), then 50 (256^3: 200) event-timed
     # ones; the headline workload last
     for name in order:
         cw, cbufs, cstep = setups[name]
         for _ in range(5):
+            cstep()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(5):
+            cstep()
+        torch.cuda.synchronize()
+        per_launch = (time.perf_counter() - t0) / 5
+        for _ in range(int(args.config_warmup / per_launch)):
             cstep()
         out["configs"][name] = {"kernel_us": event_timed(cstep, 200 if cw.m * cw.n * cw.k < 2**26 else 50),
                                 "tile": args.tile or g.select_tile(cw.m, cw.n, cw.k)}
@@ -404,7 +416,7 @@ def summarize(args, results: list) -> dict:
         cfg = {"workload": name, "m": cw.m, "n": cw.n, "k": cw.k, "values": cw.dist,
                "tile": results[0]["configs"][name]["tile"], "kernel_median_us": round(us, 2),
                "tflops": round(tf, 1), "frac": round(tf / PEAK_TFLOPS, 4),
-               "traffic": measured_traffic(name)}
+               "traffic": measured_traffic(name), "warmup_s": getattr(args, "config_warmup", None)}
         if name == w.name and "sustained" in rec:
             cfg["sustained_tflops"] = rec["sustained"]["tflops"]
         elif all("sustained" in r["configs"][name] for r in results):
@@ -432,6 +444,8 @@ def main() -> int:
                     help="seconds of back-to-back headline GEMMs per process (0 = skip)")
     ap.add_argument("--config-sustain", type=float, default=1.0,
                     help="seconds of back-to-back launches of each other workload (0: skip)")
+    ap.add_argument("--config-warmup", type=float, default=0.1,
+                    help="seconds of back-to-back warm-up launches before each workload's event-timed ones")
     ap.add_argument("--cpu-budget", type=float, default=15.0,
                     help="seconds of oracle work for the CPU baseline (0 = skip it and the parity checks)")
     ap.add_argument("--traffic-calibration", type=int, default=0, metavar="BYTES",
@@ -484,7 +498,8 @@ def main() -> int:
             cmd = [sys.executable, os.path.abspath(__file__), "--child", tmp, "--index", str(i),
                    "--steps", str(args.steps), "--warmup", str(args.warmup), "--workload", args.workload,
                    "--tile", str(args.tile), "--swizzle", str(args.swizzle), "--xcd", str(args.xcd),
-                   "--sustain", str(args.sustain), "--config-sustain", str(args.config_sustain)]
+                   "--sustain", str(args.sustain), "--config-sustain", str(args.config_sustain),
+                   "--config-warmup", str(args.config_warmup)]
             rc = subprocess.run(cmd).returncode
             if rc != 0:
                 log(f"child {i} failed with status {rc}")
