@@ -14,18 +14,15 @@ launches back to back for at least --config-warmup seconds (at least 5;
 the clock takes milliseconds to settle after the load changes, and 0.1 s
 and 0.3 s give the same figures), then 50 event-timed launches, 200 for the
 launch-bound 256^3.  Then, for the headline workload, it runs W untimed
-warm-up GEMMs and
-exactly K timed GEMMs between two device synchronisations, every launch
-also bracketed by HIP events on the stream it runs on (the kernel's average
-duration, for the roofline figure); then a sustained run of back-to-back
-GEMMs for at least --sustain seconds, a cold-cache figure (a 512 MiB
-buffer written before each launch), and last each other workload back to
-back for at least --config-sustain seconds ("sustained_tflops" in
-`configs`: the clock needs milliseconds to settle after the load changes,
-so the 50-launch figures of the shorter workloads catch it still moving).
-`value` is the median over the
-children of the headline's K-step wall-clock rate; the per-workload figures
-are medians too.  The headline thus runs on a device at its operating
+warm-up GEMMs and exactly K timed GEMMs between two device
+synchronisations, every launch also bracketed by HIP events on the stream
+it runs on (the kernel's average duration, for the roofline figure); then
+a sustained run of back-to-back GEMMs for at least --sustain seconds, a
+cold-cache figure (a 512 MiB buffer written before each launch), and last
+each other workload back to back for at least --config-sustain seconds
+("sustained_tflops" in `configs`, the wall-clock rate, launch gaps
+included).  `value` is the median over the children of the headline's
+K-step wall-clock rate; the per-workload figures are medians too.  The headline thus runs on a device at its operating
 point; the first child also times the headline's first W + K steps on the
 device as it comes from idle ("cold_start"), which on this power-managed
 part run about a tenth slower while the clock ramps.
